@@ -1,0 +1,18 @@
+"""CPU oracle for causal softmax attention, forward and backward.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import or call anything here.  The GPU
+library never uses it, and it uses nothing of the GPU library.
+
+Every function is pinned by CPU tests (``tests/test_oracle_pins.py``) against
+results fixed independently of this code: pure-Python brute force, float64
+central differences, closed forms, invariants and torch's own CPU
+scaled-dot-product attention.  No function here is "parity unpinned".
+"""
+
+from .attention import (  # noqa: F401
+    attention_backward,
+    attention_backward_head,
+    attention_forward,
+    attention_forward_head,
+)
