@@ -1,0 +1,222 @@
+"""Throughput of the fused causal attention path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+One step is one pass of the whole path over one batch: xfa_fwd, then
+xfa_bwd_preprocess, then xfa_bwd, with inputs resident in HBM.  The default
+workload is causal bf16 attention, B=8, H=16, S=4096, hd=128.  The printed
+JSON line carries the whole-step throughput in algorithmic TFLOP/s (only
+unmasked query/key pairs count: 4*hd flop per pair forward, 10*hd backward),
+each kernel's average duration from HIP events recorded on the stream the
+kernels run on, the roofline of the dominant kernel, and the CPU oracle timed
+on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402
+
+METRIC = "causal attention fwd+bwd TFLOP/s at 1 MI355X (and % of MFMA peak)"
+PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # MI355X dense MFMA peaks
+PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SRC = {
+    "bwd": "transformer_attention_xfa_amd/csrc/xfa_bwd.hip",
+    "fwd": "transformer_attention_xfa_amd/csrc/xfa_fwd.hip",
+    "pre": "transformer_attention_xfa_amd/csrc/xfa_pre.hip",
+}
+KERNEL_NAME = {"fwd": "fwd_kernel", "pre": "bwd_pre_kernel", "bwd": "bwd_kernel"}
+
+
+def source_digest(phase: str) -> str:
+    h = hashlib.sha256()
+    for rel in (KERNEL_SRC[phase], "transformer_attention_xfa_amd/csrc/xfa_common.h"):
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(phase: str, w) -> float | None:
+    """HBM bytes per launch from the committed counter runs, if they were
+    taken on the current kernel source and this workload; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f).get(phase)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_digest") != source_digest(phase) or rec.get("workload") != w.name:
+        return None
+    return float(rec["hbm_bytes_per_launch"])
+
+
+def gpu_bench(x, steps: int, warmup: int):
+    import torch
+
+    import transformer_attention_xfa_amd as xfa
+
+    w = x.w
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    if w.dtype == "bf16":
+        q, k, v, do = (torch.from_numpy(getattr(x, n + "_bits").view(np.int16)).view(torch.bfloat16).to(dev)
+                       for n in ("q", "k", "v", "do"))
+    else:
+        q, k, v, do = (torch.from_numpy(getattr(x, n)).to(dev) for n in ("q", "k", "v", "do"))
+    B, H, S, hd = w.shape
+    out = torch.empty_like(q)
+    lse = torch.empty((B, H, S), dtype=torch.float32, device=dev)
+    delta = torch.empty_like(lse)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    ws = xfa.workspace_for(q)
+    scale, causal = w.sm_scale, w.causal
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        xfa.xfa_fwd(q, k, v, out, lse, scale, causal, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        xfa.xfa_bwd_preprocess(out, do, delta, ws, scale, causal, stream)
+        if ev is not None:
+            ev[2].record(stream)
+        xfa.xfa_bwd(q, k, v, do, lse, delta, dq, dk, dv, ws, scale, causal, stream)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for _ in range(warmup):
+        step()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = {"fwd": [], "pre": [], "bwd": []}
+    for ev in events:
+        ms["fwd"].append(ev[0].elapsed_time(ev[1]))
+        ms["pre"].append(ev[1].elapsed_time(ev[2]))
+        ms["bwd"].append(ev[2].elapsed_time(ev[3]))
+    assert torch.isfinite(out).all() and torch.isfinite(dq).all(), "non-finite output"
+    name = torch.cuda.get_device_name(dev)
+    return (t1 - t0) * 1e3 / steps, {p: float(np.mean(v)) for p, v in ms.items()}, \
+        {p: float(np.median(v)) for p, v in ms.items()}, name
+
+
+def cpu_baseline(x, n_heads: int):
+    """The oracle, untuned, on the first n_heads heads of the workload (fwd + bwd)."""
+    from oracle import attention_backward_head, attention_forward_head
+
+    w = x.w
+    cores = None
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((i.get("num_threads") or 0) for i in threadpool_info()) or None
+    except Exception:
+        pass
+    heads = [[x.f64(n, h) for n in ("q", "k", "v", "do")] for h in range(n_heads)]
+    t0 = time.perf_counter()
+    for q, k, v, do in heads:
+        attention_forward_head(q, k, v, w.sm_scale, w.causal, row_block=1024)
+        attention_backward_head(q, k, v, do, w.sm_scale, w.causal, row_block=1024)
+    dt = time.perf_counter() - t0
+    flop = (w.fwd_flop + w.bwd_flop) / w.BH * n_heads
+    return {
+        "value": round(flop / dt / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": cores or os.cpu_count(),
+        "kind": "oracle",
+        "sample": f"{n_heads} of {w.BH} heads of {w.name}, forward + backward, float64 NumPy "
+                  f"composed attention (it computes all S*S products; the rate uses the same "
+                  f"algorithmic flop count as the GPU); {dt:.1f} s on {platform.processor() or platform.machine()}",
+        "seconds": round(dt, 2),
+    }
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=workloads.C4.name, choices=sorted(workloads.BY_NAME))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=32)
+    args = ap.parse_args(argv)
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the attention path is independent per head, and "
+              "sharding heads across GPUs needs no communication, so run it with --gpus 1.",
+              file=sys.stderr)
+        return 2
+
+    w = workloads.BY_NAME[args.workload]
+    x = workloads.make_inputs(w)
+    ms_step, ms_mean, ms_med, device = gpu_bench(x, args.steps, args.warmup)
+    flop = w.fwd_flop + w.bwd_flop
+    value = flop / (ms_step * 1e-3) / 1e12
+
+    # the dominant kernel: the one with the longest average duration
+    phase_flop = {"fwd": w.fwd_flop, "bwd": w.bwd_flop}
+    dom = max(("fwd", "bwd"), key=lambda p: ms_mean[p])
+    achieved = phase_flop[dom] / (ms_mean[dom] * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    roofline = {
+        "bound": "mfma", "kernel": KERNEL_NAME[dom], "achieved": round(achieved, 2), "peak": peak,
+        "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+        "traffic": measured_traffic(dom, w),
+        "avg_launch_ms": round(ms_mean[dom], 4),
+    }
+    el = 2 if w.dtype == "bf16" else 4
+    pre_bytes = w.BH * w.S * (2 * w.hd * el + 4 + w.hd * 4)   # read O, dO; write D, clear dQ acc
+    phases = {
+        "fwd": {"kernel": KERNEL_NAME["fwd"], "avg_ms": round(ms_mean["fwd"], 4), "median_ms": round(ms_med["fwd"], 4),
+                "tflops": round(w.fwd_flop / (ms_mean["fwd"] * 1e-3) / 1e12, 2)},
+        "bwd_preprocess": {"kernel": KERNEL_NAME["pre"], "avg_ms": round(ms_mean["pre"], 4),
+                           "median_ms": round(ms_med["pre"], 4),
+                           "gbs": round(pre_bytes / (ms_mean["pre"] * 1e-3) / 1e9, 1),
+                           "frac_hbm": round(pre_bytes / (ms_mean["pre"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+        "bwd": {"kernel": KERNEL_NAME["bwd"], "avg_ms": round(ms_mean["bwd"], 4), "median_ms": round(ms_med["bwd"], 4),
+                "tflops": round(w.bwd_flop / (ms_mean["bwd"] * 1e-3) / 1e12, 2)},
+    }
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "S": w.S, "hd": w.hd, "causal": w.causal,
+                   "scale": w.sm_scale, "global_batch": w.B, "seq_len": w.S, "parallelism": "none"},
+        "frac_of_peak": round(value / PEAK_TFLOPS[w.dtype], 4),
+        "roofline": roofline,
+        "phases": phases,
+        "device": device,
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(x, args.cpu_heads)
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -15,4 +15,5 @@ from .attention import (  # noqa: F401
     attention_backward_head,
     attention_forward,
     attention_forward_head,
+    attention_forward_rows,
 )

@@ -117,6 +117,23 @@ def attention_backward_head(q, k, v, dout, scale: float, causal: bool = True,
     return dq, dk, dv, dref
 
 
+def attention_forward_rows(q, k, v, rows, scale: float, causal: bool = True):
+    """One head, selected query rows only: (out ``[len(rows), hd]``, lse).
+
+    Each requested row i is the same definition as in attention_forward_head
+    (softmax over keys j <= i when causal); used to check single rows of very
+    long sequences.
+    """
+    q, k, v = (np.asarray(a, dtype=np.float64) for a in (q, k, v))
+    _check_head(q, k, v)
+    rows = np.asarray(rows, dtype=np.int64)
+    s = (q[rows] @ k.T) * scale
+    if causal:
+        s = np.where(np.arange(k.shape[0])[None, :] > rows[:, None], _NEG_INF, s)
+    p, lse = _softmax_rows(s)
+    return p @ v, lse
+
+
 def _heads(shape, heads):
     B, H, S, hd = shape
     return list(range(B * H)) if heads is None else [int(h) for h in heads]

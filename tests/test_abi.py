@@ -1,0 +1,118 @@
+"""The C-ABI library without a GPU: it loads, exports what include/xfa.h
+declares, and rejects bad arguments before making any GPU call."""
+
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import transformer_attention_xfa_amd as xfa
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "xfa.h")
+
+OK, INVAL, UNSUP = xfa.XFA_OK, xfa.XFA_ERR_INVALID_ARGUMENT, xfa.XFA_ERR_UNSUPPORTED
+A = 0x10000  # a 16-byte-aligned non-null address; never dereferenced by these calls
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(xfa_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared()
+    assert names == sorted(["xfa_fwd", "xfa_bwd_preprocess", "xfa_bwd", "xfa_bwd_workspace_bytes",
+                            "xfa_status_string"])
+    lib = ctypes.CDLL(xfa.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    for s in (OK, INVAL, UNSUP, xfa.XFA_ERR_HIP):
+        assert xfa.xfa_status_string(s).startswith("xfa: ")
+    assert "unknown" in xfa.xfa_status_string(99)
+
+
+def _fwd(**kw):
+    a = dict(q=A, k=A, v=A, out=A, lse=A, B=1, H=2, S=64, hd=64, scale=0.125, causal=1, dtype=1)
+    a.update(kw)
+    return xfa.lib().xfa_fwd(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"], a["H"], a["S"],
+                             a["hd"], a["scale"], a["causal"], a["dtype"], None)
+
+
+def _pre(**kw):
+    a = dict(out=A, dout=A, delta=A, ws=A, B=1, H=2, S=64, hd=64, scale=0.125, causal=1, dtype=1)
+    a.update(kw)
+    return xfa.lib().xfa_bwd_preprocess(a["out"], a["dout"], a["delta"], a["ws"], a["B"], a["H"],
+                                        a["S"], a["hd"], a["scale"], a["causal"], a["dtype"], None)
+
+
+def _bwd(**kw):
+    a = dict(q=A, k=A, v=A, dout=A, lse=A, delta=A, dq=A, dk=A, dv=A, ws=A,
+             B=1, H=2, S=64, hd=64, scale=0.125, causal=1, dtype=1)
+    a.update(kw)
+    return xfa.lib().xfa_bwd(a["q"], a["k"], a["v"], a["dout"], a["lse"], a["delta"], a["dq"],
+                             a["dk"], a["dv"], a["ws"], a["B"], a["H"], a["S"], a["hd"], a["scale"],
+                             a["causal"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("call", [_fwd, _pre, _bwd])
+def test_rejects_bad_arguments(call):
+    assert call(dtype=2) == INVAL
+    assert call(dtype=-1) == INVAL
+    assert call(B=-1) == INVAL
+    assert call(S=-5) == INVAL
+    assert call(hd=0) == INVAL
+    assert call(hd=48) == UNSUP
+    assert call(hd=256) == UNSUP
+    assert call(scale=0.0) == INVAL
+    assert call(scale=-1.0) == INVAL
+    assert call(scale=math.nan) == INVAL
+    assert call(scale=math.inf) == INVAL
+    assert call(causal=2) == INVAL
+    assert call(S=(1 << 30) + 1) == UNSUP
+    assert call(B=1 << 40, H=1 << 30) == UNSUP
+
+
+@pytest.mark.parametrize("call,ptrs", [
+    (_fwd, ["q", "k", "v", "out", "lse"]),
+    (_pre, ["out", "dout", "delta", "ws"]),
+    (_bwd, ["q", "k", "v", "dout", "lse", "delta", "dq", "dk", "dv", "ws"]),
+])
+def test_rejects_null_and_misaligned_pointers(call, ptrs):
+    for p in ptrs:
+        assert call(**{p: None}) == INVAL, p
+        assert call(**{p: A + 8}) == INVAL, p
+
+
+def _round256(n):
+    return (n + 255) // 256 * 256
+
+
+def test_workspace_bytes():
+    # fp32 dQ accumulator plus one 4-byte counter per (head, 64-query tile),
+    # the counters padded to 256 bytes
+    assert xfa.xfa_bwd_workspace_bytes(8, 16, 4096, 128, xfa.XFA_DTYPE_BF16) == \
+        8 * 16 * 4096 * 128 * 4 + _round256(8 * 16 * 64 * 4)
+    assert xfa.xfa_bwd_workspace_bytes(2, 4, 256, 64, xfa.XFA_DTYPE_F32) == \
+        8 * 256 * 64 * 4 + _round256(8 * 4 * 4)
+    assert xfa.xfa_bwd_workspace_bytes(1, 1, 100, 16, xfa.XFA_DTYPE_BF16) == 100 * 16 * 4 + 256
+    assert xfa.xfa_bwd_workspace_bytes(2, 4, 256, 48, xfa.XFA_DTYPE_BF16) == 0
+    assert xfa.xfa_bwd_workspace_bytes(0, 4, 256, 64, xfa.XFA_DTYPE_BF16) == 0
+    assert xfa.xfa_bwd_workspace_bytes(1, 1, 8, 64, 7) == 0
+
+
+@pytest.mark.parametrize("call", [_fwd, _pre, _bwd])
+def test_empty_problem_is_a_no_op(call):
+    # nothing to do: succeeds without touching (null) pointers or the GPU
+    nulls = {"fwd": ["q", "k", "v", "out", "lse"], "pre": ["out", "dout", "delta", "ws"],
+             "bwd": ["q", "k", "v", "dout", "lse", "delta", "dq", "dk", "dv", "ws"]}
+    key = call.__name__[1:]
+    args = {p: None for p in nulls[key]}
+    assert call(S=0, **args) == OK
+    assert call(B=0, **args) == OK
+    assert call(H=0, **args) == OK

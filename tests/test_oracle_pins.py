@@ -18,7 +18,7 @@ import numpy as np
 import pytest
 
 from oracle import (attention_backward, attention_backward_head, attention_forward,
-                    attention_forward_head)
+                    attention_forward_head, attention_forward_rows)
 
 RNG = np.random.default_rng(12345)
 
@@ -302,3 +302,15 @@ def test_batched_heads_independent():
     ref = attention_backward_head(q[1, 1], k[1, 1], v[1, 1], do[1, 1], 0.5, True)
     for x, y in zip(bw[4], ref):
         np.testing.assert_array_equal(x, y)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_selected_rows(causal):
+    S, hd = 8, 3
+    rng = np.random.default_rng(77)
+    q, k, v, do = (_rand(S, hd, rng=rng) for _ in range(4))
+    rows = [7, 0, 3, 3, 5]
+    out, lse = attention_forward_rows(q, k, v, rows, 0.6, causal)
+    b_out, b_lse, *_ = _brute(q, k, v, do, 0.6, causal)
+    np.testing.assert_allclose(out, b_out[rows], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, b_lse[rows], rtol=0, atol=1e-12)

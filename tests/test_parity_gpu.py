@@ -1,0 +1,264 @@
+"""GPU parity: the HIP path, called through the C ABI, against the CPU oracle.
+
+Both sides get identical seeded inputs from ``workloads``.  Tolerances:
+  * fp32 workloads: max |out - ref| <= 1e-5, max |L - ref| <= 1e-5, and per
+    gradient tensor max |g - ref| / max |ref| <= 1e-4;
+  * bf16 workloads: max |out - ref| <= 2e-2, max |L - ref| <= 2e-2, and per
+    gradient tensor ||g - ref||_2 / ||ref||_2 <= 5e-2.
+Where a gradient is exactly zero (one key, S = 1) the relative measures have
+no scale of their own: there dp - D cancels two independently rounded O(1)
+dot products.  Their denominators are floored (fp32: max |ref| at 1e-2; bf16:
+the root mean square of ref at 1e-3), one to two orders below the gradients'
+magnitude for the unit-variance inputs used here.
+D is checked against the oracle's row sums of P * dP, with the slack that the
+stored O's own error allows.  At the full sizes the oracle runs on sampled
+heads (every element of those heads) and properties that hold at any size are
+checked on every head.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+import workloads
+from oracle import attention_backward_head, attention_forward_head, attention_forward_rows
+
+torch = pytest.importorskip("torch")
+import transformer_attention_xfa_amd as xfa  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+TOL_F32 = dict(out=1e-5, lse=1e-5, grad=1e-4)
+TOL_BF16 = dict(out=2e-2, lse=2e-2, grad=5e-2)
+
+
+def say(msg):
+    print(f"[gpu] {msg}", flush=True)
+
+
+def to_dev(x, name, stream=None):
+    if x.w.dtype == "bf16":
+        bits = getattr(x, name + "_bits")
+        t = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(getattr(x, name))
+    return t.to("cuda")
+
+
+def host(t):
+    return t.float().cpu().numpy()
+
+
+def run_gpu(x, stream=None):
+    """Forward, preprocess and backward through the C ABI; host copies (fp32)."""
+    w = x.w
+    say(f"run {w.name} B={w.B} H={w.H} S={w.S} hd={w.hd} {w.dtype} causal={w.causal}")
+    q, k, v, do = (to_dev(x, n) for n in ("q", "k", "v", "do"))
+    B, H, S, hd = w.shape
+    out = torch.empty_like(q)
+    lse = torch.empty((B, H, S), dtype=torch.float32, device="cuda")
+    delta = torch.empty_like(lse)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    ws = xfa.workspace_for(q)
+    ctx = torch.cuda.stream(stream) if stream is not None else torch.cuda.stream(torch.cuda.current_stream())
+    with ctx:
+        xfa.xfa_fwd(q, k, v, out, lse, w.sm_scale, w.causal)
+        xfa.xfa_bwd_preprocess(out, do, delta, ws, w.sm_scale, w.causal)
+        xfa.xfa_bwd(q, k, v, do, lse, delta, dq, dk, dv, ws, w.sm_scale, w.causal)
+    torch.cuda.synchronize()
+    res = {n: host(t) for n, t in dict(out=out, lse=lse, delta=delta, dq=dq, dk=dk, dv=dv).items()}
+    del q, k, v, do, out, lse, delta, dq, dk, dv, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def head(a, w, bh):
+    return a.reshape(w.BH, w.S, *a.shape[3:])[bh].astype(np.float64)
+
+
+def compare_head(x, g, bh, row_block=None):
+    """Every element of head bh against the oracle; returns the error metrics."""
+    w = x.w
+    q, k, v, do = (x.f64(n, bh) for n in ("q", "k", "v", "do"))
+    out_r, lse_r = attention_forward_head(q, k, v, w.sm_scale, w.causal, row_block)
+    dq_r, dk_r, dv_r, dref = attention_backward_head(q, k, v, do, w.sm_scale, w.causal, row_block)
+    tol = TOL_F32 if w.dtype == "f32" else TOL_BF16
+    out, lse, delta = head(g["out"], w, bh), head(g["lse"], w, bh), head(g["delta"], w, bh)
+    m = {"out": np.abs(out - out_r).max(), "lse": np.abs(lse - lse_r).max()}
+    assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
+    for n, ref in (("dq", dq_r), ("dk", dk_r), ("dv", dv_r)):
+        got = head(g[n], w, bh)
+        assert np.all(np.isfinite(got)), n
+        if w.dtype == "f32":
+            m[n] = np.abs(got - ref).max() / max(np.abs(ref).max(), 1e-2)
+        else:
+            m[n] = np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-3 * math.sqrt(ref.size))
+    # D: exact row sums up to the error the stored O carries
+    slack = np.abs(do).sum(axis=1) * tol["out"] + 1e-5 * (1 + np.abs(dref))
+    m["delta"] = np.abs(delta - dref).max()
+    assert np.all(np.abs(delta - dref) <= slack), f"D off by {m['delta']}"
+    say(f"{w.name} head {bh}: " + " ".join(f"{n}={v:.3g}" for n, v in m.items()))
+    assert m["out"] <= tol["out"], m
+    assert m["lse"] <= tol["lse"], m
+    for n in ("dq", "dk", "dv"):
+        assert m[n] <= tol["grad"], m
+    return m
+
+
+def check_invariants(x, g):
+    """Per head: sum_j dK_j = 0, sum_j dV_j = sum_i dO_i, Q^T dQ = dK^T K."""
+    w = x.w
+    worst = dict(dk_sum=0.0, dv_sum=0.0, qdq=0.0)
+    for bh in range(w.BH):
+        q, k, do = x.f64("q", bh), x.f64("k", bh), x.f64("do", bh)
+        dq, dk, dv = head(g["dq"], w, bh), head(g["dk"], w, bh), head(g["dv"], w, bh)
+        worst["dk_sum"] = max(worst["dk_sum"], np.linalg.norm(dk.sum(0)) / np.linalg.norm(dk))
+        worst["dv_sum"] = max(worst["dv_sum"],
+                              np.linalg.norm(dv.sum(0) - do.sum(0)) / np.linalg.norm(do.sum(0)))
+        a, b = q.T @ dq, dk.T @ k
+        worst["qdq"] = max(worst["qdq"], np.linalg.norm(a - b) / np.linalg.norm(b))
+    say(f"{w.name} invariants over {w.BH} heads: " + " ".join(f"{n}={v:.3g}" for n, v in worst.items()))
+    lim = 1e-4 if w.dtype == "f32" else 5e-2
+    assert worst["dk_sum"] <= lim and worst["dv_sum"] <= lim and worst["qdq"] <= lim, worst
+
+
+_CACHE = {}
+
+
+def gpu_result(w):
+    if w.name not in _CACHE:
+        x = workloads.make_inputs(w)
+        _CACHE.clear()
+        _CACHE[w.name] = (x, run_gpu(x))
+    return _CACHE[w.name]
+
+
+# ------------------------------------------------------------- the workloads
+@pytest.mark.parametrize("w", [workloads.C1, workloads.C2, workloads.C3], ids=lambda w: w.name)
+def test_small_workloads_every_head(w):
+    x, g = gpu_result(w)
+    for bh in range(w.BH):
+        compare_head(x, g, bh)
+    check_invariants(x, g)
+
+
+def test_c4_sampled_heads_and_invariants():
+    w = workloads.C4
+    x, g = gpu_result(w)
+    for bh in (0, 77, w.BH - 1):
+        compare_head(x, g, bh)
+    check_invariants(x, g)
+
+
+def test_c5_one_head():
+    w = workloads.C5
+    x, g = gpu_result(w)
+    compare_head(x, g, 13, row_block=2048)
+
+
+def test_c5_lse_stability_and_invariants():
+    w = workloads.C5
+    x, g = gpu_result(w)
+    assert np.all(np.isfinite(g["lse"])) and np.all(np.isfinite(g["out"]))
+    rng = np.random.default_rng(0)
+    for bh in (0, 31):
+        q, k, v = x.f64("q", bh), x.f64("k", bh), x.f64("v", bh)
+        lse = head(g["lse"], w, bh)
+        worst = 0.0
+        for r0 in range(0, w.S, 2048):
+            s = (q[r0:r0 + 2048] @ k.T) * w.sm_scale
+            rows = np.arange(r0, min(r0 + 2048, w.S))
+            s[np.arange(w.S)[None, :] > rows[:, None]] = -np.inf
+            mx = s.max(axis=1)
+            lo = mx - lse[rows]
+            hi = lse[rows] - mx - np.log(rows + 1.0)
+            worst = max(worst, lo.max(), hi.max())
+        say(f"{w.name} head {bh}: logsumexp bound violation {worst:.3g}")
+        assert worst <= 1e-3
+        rows = np.sort(rng.choice(w.S, 64, replace=False))
+        out_r, lse_r = attention_forward_rows(q, k, v, rows, w.sm_scale, True)
+        assert np.abs(head(g["out"], w, bh)[rows] - out_r).max() <= TOL_BF16["out"]
+        assert np.abs(lse[rows] - lse_r).max() <= TOL_BF16["lse"]
+    check_invariants(x, g)
+
+
+@pytest.mark.parametrize("w", workloads.PAGE_SHAPES, ids=lambda w: w.name)
+def test_page_shapes(w):
+    x, g = gpu_result(w)
+    for bh in (0, w.BH - 1):
+        compare_head(x, g, bh)
+    check_invariants(x, g)
+
+
+# ---------------------------------------------------------------- edge cases
+EDGE_S = [1, 17, 64, 100, 129, 300]
+
+
+@pytest.mark.parametrize("causal", [True, False], ids=["causal", "full"])
+@pytest.mark.parametrize("hd", [16, 32, 64, 128])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_edge_shapes(dtype, hd, causal):
+    for S in EDGE_S:
+        w = workloads.Workload(f"edge_{dtype}_hd{hd}_s{S}_{'c' if causal else 'f'}", dtype, 1, 2, S, hd,
+                               seed=1000 + S + hd, causal=causal, do_std=1.0 if dtype == "f32" else 0.1)
+        x = workloads.make_inputs(w)
+        g = run_gpu(x)
+        for bh in range(w.BH):
+            compare_head(x, g, bh)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_zero_query_is_uniform_attention(dtype):
+    # Q = 0: out_i is the mean of V_0..V_i and L_i = ln(i+1)
+    w = workloads.Workload(f"zeroq_{dtype}", dtype, 1, 2, 200, 64, seed=7)
+    x = workloads.make_inputs(w)
+    x.q[...] = 0.0
+    if x.q_bits is not None:
+        x.q_bits[...] = 0
+    g = run_gpu(x)
+    for bh in range(w.BH):
+        compare_head(x, g, bh)
+        lse = head(g["lse"], w, bh)
+        np.testing.assert_allclose(lse, np.log(np.arange(1, w.S + 1)), rtol=0, atol=1e-5)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_peaky_logits(dtype):
+    # logits with standard deviation 4 (fp32) / 16 (bf16).  fp32 rounding of a
+    # 64-term dot product grows with the logits' size; at std 4 it stays well
+    # inside the fp32 tolerance.
+    std = 2.0 if dtype == "f32" else 4.0
+    w = workloads.Workload(f"peaky_{dtype}", dtype, 1, 2, 257, 64, seed=8, q_std=std, k_std=std,
+                           do_std=1.0 if dtype == "f32" else 0.1)
+    x = workloads.make_inputs(w)
+    g = run_gpu(x)
+    for bh in range(w.BH):
+        compare_head(x, g, bh)
+
+
+def test_nondefault_stream_and_repeatability():
+    w = workloads.C3.with_(B=1, H=4)
+    x = workloads.make_inputs(w)
+    g0 = run_gpu(x)
+    s = torch.cuda.Stream()
+    g1 = run_gpu(x, stream=s)
+    for n in ("out", "lse", "delta", "dk", "dv"):
+        np.testing.assert_array_equal(g0[n], g1[n], err_msg=n)
+    # dQ is summed with atomics: the order may change its rounding
+    diff = np.abs(g0["dq"] - g1["dq"]).max()
+    say(f"dq run-to-run max difference {diff:.3g}")
+    for bh in range(w.BH):
+        compare_head(x, g1, bh)
+
+
+def test_empty_and_error_paths():
+    q = torch.zeros((1, 1, 0, 64), dtype=torch.bfloat16, device="cuda")
+    out, lse = xfa.forward(q, q, q)
+    assert out.shape == q.shape and lse.shape == (1, 1, 0)
+    q = torch.zeros((1, 1, 8, 48), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(xfa.XfaError):
+        xfa.forward(q, q, q)
+    q = torch.zeros((1, 1, 8, 64), dtype=torch.float16, device="cuda")
+    with pytest.raises(TypeError):
+        xfa.forward(q, q, q)

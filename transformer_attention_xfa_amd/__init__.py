@@ -1,0 +1,25 @@
+"""MI355X-native fused causal flash-attention, forward and backward.
+
+The computation lives in libxfa.so (hand-written HIP for gfx950, C ABI in
+include/xfa.h); this package is its thin Python binding.
+"""
+
+from ._binding import (  # noqa: F401
+    LIB_PATH,
+    XFA_DTYPE_BF16,
+    XFA_DTYPE_F32,
+    XFA_ERR_HIP,
+    XFA_ERR_INVALID_ARGUMENT,
+    XFA_ERR_UNSUPPORTED,
+    XFA_OK,
+    XfaError,
+    backward,
+    forward,
+    lib,
+    workspace_for,
+    xfa_bwd,
+    xfa_bwd_preprocess,
+    xfa_bwd_workspace_bytes,
+    xfa_fwd,
+    xfa_status_string,
+)

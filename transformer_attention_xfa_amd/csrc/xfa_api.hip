@@ -1,0 +1,108 @@
+// C-ABI layer of libxfa.so: argument checks, then kernel launches on the
+// caller's stream.  Declarations and the full contract are in xfa.h.
+#include <math.h>
+#include <stdint.h>
+
+#include "xfa.h"
+#include "xfa_launch.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Shape {
+  int64_t BH = 0, S = 0, hd = 0;
+  bool empty = false;
+  bool bf16 = false;
+};
+
+// Checks shared by every entry point; fills `sh` on success.
+xfa_status_t check_common(int64_t B, int64_t H, int64_t S, int64_t hd, float scale, int causal,
+                          int dtype, Shape* sh) {
+  if (dtype != XFA_DTYPE_F32 && dtype != XFA_DTYPE_BF16) return XFA_ERR_INVALID_ARGUMENT;
+  if (B < 0 || H < 0 || S < 0 || hd <= 0) return XFA_ERR_INVALID_ARGUMENT;
+  if (!(isfinite(scale) && scale > 0.f)) return XFA_ERR_INVALID_ARGUMENT;
+  if (causal != 0 && causal != 1) return XFA_ERR_INVALID_ARGUMENT;
+  if (hd != 16 && hd != 32 && hd != 64 && hd != 128) return XFA_ERR_UNSUPPORTED;
+  // the kernels index positions with int and launch one workgroup per
+  // (head, 32..128-row tile) on a 1-D grid
+  if (S > (int64_t(1) << 30)) return XFA_ERR_UNSUPPORTED;
+  if (B > 0 && H > INT64_MAX / B) return XFA_ERR_UNSUPPORTED;
+  const int64_t BH = B * H;
+  if (BH > 0 && (S + 31) / 32 > int64_t(INT32_MAX) / BH) return XFA_ERR_UNSUPPORTED;
+  sh->BH = BH;
+  sh->S = S;
+  sh->hd = hd;
+  sh->empty = (BH == 0 || S == 0);
+  sh->bf16 = dtype == XFA_DTYPE_BF16;
+  return XFA_OK;
+}
+
+xfa_status_t check_ptrs(std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (p == nullptr || !aligned16(p)) return XFA_ERR_INVALID_ARGUMENT;
+  return XFA_OK;
+}
+
+xfa_status_t from_hip(hipError_t e) { return e == hipSuccess ? XFA_OK : XFA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+xfa_status_t xfa_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+                     int64_t B, int64_t H, int64_t S, int64_t hd, float scale, int causal,
+                     int dtype, void* stream) {
+  Shape sh;
+  xfa_status_t st = check_common(B, H, S, hd, scale, causal, dtype, &sh);
+  if (st != XFA_OK || sh.empty) return st;
+  if ((st = check_ptrs({q, k, v, out, lse})) != XFA_OK) return st;
+  xfa::FwdArgs a{q, k, v, out, lse, sh.BH, sh.S, sh.hd, scale, causal, sh.bf16, (hipStream_t)stream};
+  return from_hip(xfa::launch_fwd(a));
+}
+
+xfa_status_t xfa_bwd_preprocess(const void* out, const void* dout, float* delta, void* workspace,
+                                int64_t B, int64_t H, int64_t S, int64_t hd, float scale,
+                                int causal, int dtype, void* stream) {
+  Shape sh;
+  xfa_status_t st = check_common(B, H, S, hd, scale, causal, dtype, &sh);
+  if (st != XFA_OK || sh.empty) return st;
+  if ((st = check_ptrs({out, dout, delta, workspace})) != XFA_OK) return st;
+  xfa::Workspace ws;
+  xfa::bwd_workspace(workspace, sh.BH, sh.S, sh.hd, sh.bf16, &ws);
+  xfa::PreArgs a{out, dout, delta, ws, sh.BH, sh.S, sh.hd, sh.bf16, (hipStream_t)stream};
+  return from_hip(xfa::launch_bwd_preprocess(a));
+}
+
+size_t xfa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t S, int64_t hd, int dtype) {
+  Shape sh;
+  if (check_common(B, H, S, hd, 1.f, 1, dtype, &sh) != XFA_OK || sh.empty) return 0;
+  return xfa::bwd_workspace(nullptr, sh.BH, sh.S, sh.hd, sh.bf16, nullptr);
+}
+
+xfa_status_t xfa_bwd(const void* q, const void* k, const void* v, const void* dout,
+                     const float* lse, const float* delta, void* dq, void* dk, void* dv,
+                     void* workspace, int64_t B, int64_t H, int64_t S, int64_t hd, float scale,
+                     int causal, int dtype, void* stream) {
+  Shape sh;
+  xfa_status_t st = check_common(B, H, S, hd, scale, causal, dtype, &sh);
+  if (st != XFA_OK || sh.empty) return st;
+  if ((st = check_ptrs({q, k, v, dout, lse, delta, dq, dk, dv, workspace})) != XFA_OK) return st;
+  xfa::Workspace ws;
+  xfa::bwd_workspace(workspace, sh.BH, sh.S, sh.hd, sh.bf16, &ws);
+  xfa::BwdArgs a{q, k, v, dout, lse, delta, dq, dk, dv, ws,
+                 sh.BH, sh.S, sh.hd, scale, causal, sh.bf16, (hipStream_t)stream};
+  return from_hip(xfa::launch_bwd(a));
+}
+
+const char* xfa_status_string(xfa_status_t s) {
+  switch (s) {
+    case XFA_OK: return "xfa: ok";
+    case XFA_ERR_INVALID_ARGUMENT: return "xfa: invalid argument";
+    case XFA_ERR_UNSUPPORTED: return "xfa: unsupported size";
+    case XFA_ERR_HIP: return "xfa: HIP launch failed";
+  }
+  return "xfa: unknown status";
+}
+
+}  // extern "C"
