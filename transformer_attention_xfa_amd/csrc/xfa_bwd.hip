@@ -10,29 +10,33 @@
 // owned dK/dV pass, Key Design Decisions / escape hatches): one workgroup per
 // (head, tile of 32*NW keys); wave w owns 32 keys and keeps their dK and dV in
 // registers for the whole sweep over query tiles, starting at the first query
-// tile that reaches the diagonal.  Per query tile each wave computes
+// tile that reaches the diagonal.  Per 32-query block each wave computes
 // S = Q . K^T and dP = dO . V^T with the lane owning one key, so that
 // dV^T += dO^T . P and dK^T += Q^T . dS take P and dS straight from registers
 // (dO^T and Q^T come from the row-major LDS tiles by the transpose read).  dS
 // is then passed through LDS so that the workgroup forms dQ = dS . K for the
 // tile over all of its keys, and adds it into an fp32 dQ accumulator with
-// atomics (one add per element per key tile, not per key).  When a workgroup
-// is done it publishes its additions and counts itself in on every query tile
-// it touched; the workgroup that completes a tile's count writes that tile of
-// dq in the output type.  Nothing ever waits on another workgroup.
+// atomics (one add per element per key tile, not per key).  Query tiles are
+// double-buffered in LDS: the next tile is staged while dQ is formed, so an
+// iteration has two barriers.
+//
+// The factor `scale` of ds is applied once at the end instead of per pair:
+// dK is scaled when written, and the dQ accumulator when it is converted.
+// When a workgroup is done it publishes its dQ additions and counts itself in
+// on every query tile it touched; the workgroup that completes a tile's count
+// writes that tile of dq in the output type.  Nothing waits on another
+// workgroup.
 #include "xfa_common.h"
 #include "xfa_launch.h"
 
 namespace xfa {
-
-__device__ inline void atomic_add_f32(float* p, float v) { unsafeAtomicAdd(p, v); }
 
 template <typename T, int HD, int NW, int BQ>
 __global__ __launch_bounds__(NW * 64, 1) void bwd_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const T* __restrict__ dO, const float* __restrict__ Lse, const float* __restrict__ Dl,
     T* __restrict__ dQ, T* __restrict__ dK, T* __restrict__ dV, float* __restrict__ dQacc,
-    unsigned* __restrict__ counters, int S, float scale, float scale_log2, int causal, int nkt,
+    unsigned* __restrict__ counters, int S, float scale, float c_log2, int causal, int nkt,
     int nwg) {
   using M = Mma<T>;
   constexpr int BKV = NW * 32;                   // keys per workgroup
@@ -51,15 +55,16 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_kernel(
   constexpr int PF = (QCH + NT - 1) / NT;
   constexpr int NOB = NQB * NDB;                 // dQ output blocks per query tile
   constexpr int OBW = (NOB + NW - 1) / NW;       // dQ output blocks per wave
+  constexpr uint32_t ROWB = HD * sizeof(T);
   static_assert(HD % M::KD == 0 && HD % VE == 0, "unsupported head dim");
   static_assert(BQ <= NT, "L/D staging assumes one thread per query");
 
-  __shared__ __attribute__((aligned(16))) T Qs[BQ * QLD];
-  __shared__ __attribute__((aligned(16))) T dOs[BQ * QLD];
+  __shared__ __attribute__((aligned(16))) T Qs[2][BQ * QLD];
+  __shared__ __attribute__((aligned(16))) T dOs[2][BQ * QLD];
   __shared__ __attribute__((aligned(16))) T Ks[BKV * QLD];
   __shared__ __attribute__((aligned(16))) T dSs[BKV * SLD];
-  __shared__ __attribute__((aligned(16))) float Ls[BQ];
-  __shared__ __attribute__((aligned(16))) float Ds[BQ];
+  __shared__ __attribute__((aligned(16))) float Ls[2][BQ];
+  __shared__ __attribute__((aligned(16))) float Ds[2][BQ];
   __shared__ int last_of[NT];
 
   const int tid = threadIdx.x;
@@ -74,11 +79,14 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_kernel(
   const int kt = lid - bh * nkt;
 
   const size_t hoff = (size_t)bh * S * HD;
-  const T* Qh = Q + hoff;
-  const T* dOh = dO + hoff;
-  const float* Lh = Lse + (size_t)bh * S;
-  const float* Dh = Dl + (size_t)bh * S;
-  float* dQh = dQacc + hoff;
+  const uint32_t head_bytes = (uint32_t)S * ROWB;
+  const rsrc_t rQ = make_rsrc(Q + hoff, head_bytes);
+  const rsrc_t rK = make_rsrc(K + hoff, head_bytes);
+  const rsrc_t rV = make_rsrc(V + hoff, head_bytes);
+  const rsrc_t rdO = make_rsrc(dO + hoff, head_bytes);
+  const rsrc_t rL = make_rsrc(Lse + (size_t)bh * S, (uint32_t)S * 4u);
+  const rsrc_t rD = make_rsrc(Dl + (size_t)bh * S, (uint32_t)S * 4u);
+  const rsrc_t rAcc = make_rsrc(dQacc + hoff, (uint32_t)S * HD * 4u);
 
   const int j0 = kt * BKV;                       // first key of the workgroup
   const int jw0 = j0 + 32 * w;                   // first key of this wave
@@ -86,13 +94,16 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_kernel(
   const bool wave_live = jw0 < S;
   const int nqt = (S + BQ - 1) / BQ;
   const int qt_first = causal ? j0 / BQ : 0;
+  // queries that see this lane's key: [q_lo, q_hi)
+  const int q_lo = causal ? kj : 0;
+  const int q_hi = kj < S ? S : 0;
 
   // zero the padding columns once; stage the workgroup's K tile (B operand of dQ)
   if constexpr (HDP != HD) {
     for (int e = tid; e < BQ * (HDP - HD); e += NT) {
       const int r = e / (HDP - HD), c = HD + e % (HDP - HD);
-      Qs[r * QLD + c] = (T)0.f;
-      dOs[r * QLD + c] = (T)0.f;
+      Qs[0][r * QLD + c] = Qs[1][r * QLD + c] = (T)0.f;
+      dOs[0][r * QLD + c] = dOs[1][r * QLD + c] = (T)0.f;
     }
     for (int e = tid; e < BKV * (HDP - HD); e += NT) {
       const int r = e / (HDP - HD), c = HD + e % (HDP - HD);
@@ -101,22 +112,20 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_kernel(
   }
   for (int e = tid; e < BKV * CPR; e += NT) {
     const int r = e / CPR, c = (e - r * CPR) * VE;
-    const int key = j0 + r;
-    typename Vec16<T>::type x{};
-    if (key < S) x = ld16(K + hoff + (size_t)key * HD + c);
-    st16(Ks + r * QLD + c, x);
+    st16(Ks + r * QLD + c, bload16<T>(rK, (uint32_t)(j0 + r) * ROWB + c * sizeof(T)));
   }
 
   // this lane's key row of K and V: B operands of S = Q.K^T and dP = dO.V^T
   typename M::frag kf[NC], vf[NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
-    if (kj < S) {
-      kf[c] = ld_nat(K + hoff + (size_t)kj * HD + c * M::KD + M::KW * h);
-      vf[c] = ld_nat(V + hoff + (size_t)kj * HD + c * M::KD + M::KW * h);
+    const uint32_t off = (uint32_t)kj * ROWB + (c * M::KD + M::KW * h) * sizeof(T);
+    if constexpr (sizeof(T) == 2) {
+      kf[c] = bload16<bf16>(rK, off);
+      vf[c] = bload16<bf16>(rV, off);
     } else {
-      kf[c] = M::zero();
-      vf[c] = M::zero();
+      kf[c] = bload4(rK, off);
+      vf[c] = bload4(rV, off);
     }
   }
 
@@ -135,122 +144,109 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_kernel(
     for (int i = 0; i < PF; ++i) {
       const int e = tid + i * NT;
       const int r = e / CPR, c = (e - r * CPR) * VE;
-      const int q = q0 + r;
-      if (e < QCH && q < S) {
-        pq[i] = ld16(Qh + (size_t)q * HD + c);
-        pd[i] = ld16(dOh + (size_t)q * HD + c);
-      } else {
-        pq[i] = typename Vec16<T>::type{};
-        pd[i] = typename Vec16<T>::type{};
+      const uint32_t off = (uint32_t)(q0 + r) * ROWB + c * sizeof(T);
+      if (QCH % NT == 0 || e < QCH) {
+        pq[i] = bload16<T>(rQ, off);   // rows past the end read as zeros
+        pd[i] = bload16<T>(rdO, off);
       }
     }
     if (tid < BQ) {
-      const int q = q0 + tid;
-      pl = q < S ? Lh[q] * kLog2e : 0.f;
-      pdl = q < S ? Dh[q] : 0.f;
+      pl = bload4(rL, (uint32_t)(q0 + tid) * 4u) * kLog2e;
+      pdl = bload4(rD, (uint32_t)(q0 + tid) * 4u);
     }
   };
-  auto stage = [&]() {
+  auto stage = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < PF; ++i) {
       const int e = tid + i * NT;
-      if (e < QCH) {
+      if (QCH % NT == 0 || e < QCH) {
         const int r = e / CPR, c = (e - r * CPR) * VE;
-        st16(Qs + r * QLD + c, pq[i]);
-        st16(dOs + r * QLD + c, pd[i]);
+        st16(Qs[buf] + r * QLD + c, pq[i]);
+        st16(dOs[buf] + r * QLD + c, pd[i]);
       }
     }
     if (tid < BQ) {
-      Ls[tid] = pl;
-      Ds[tid] = pdl;
+      Ls[buf][tid] = pl;
+      Ds[buf][tid] = pdl;
     }
   };
 
   prefetch(qt_first);
-  for (int qt = qt_first; qt < nqt; ++qt) {
-    __syncthreads();
-    stage();
-    __syncthreads();
-    if (qt + 1 < nqt) prefetch(qt + 1);
+  stage(0);
+  __syncthreads();
+  if (qt_first + 1 < nqt) prefetch(qt_first + 1);
 
+  T* srow = dSs + (32 * w + (l & 31)) * SLD;   // this lane's key row of the dS tile
+  for (int qt = qt_first; qt < nqt; ++qt) {
+    const int buf = (qt - qt_first) & 1;
+    const T* Qb = Qs[buf];
+    const T* dOb = dOs[buf];
     const int q0 = qt * BQ;
     const int q_last = min(q0 + BQ, S) - 1;
     // keys of this wave all above the diagonal of this query tile: nothing to add
     const bool active = wave_live && !(causal && jw0 > q_last);
+    const bool need_mask = (q0 + BQ > S) || (jw0 + 32 > S) || (causal && jw0 + 31 > q0);
 
-    if (active) {
-      f32x16 sacc[NQB], pacc[NQB];
 #pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
-        sacc[qb] = zero16();
-        pacc[qb] = zero16();
-        const T* qrow = Qs + (qb * 32 + (l & 31)) * QLD + M::KW * h;
-        const T* dorow = dOs + (qb * 32 + (l & 31)) * QLD + M::KW * h;
+    for (int qb = 0; qb < NQB; ++qb) {
+      if (active) {
+        f32x16 sacc = zero16(), pacc = zero16();
+        const T* qrow = Qb + (qb * 32 + (l & 31)) * QLD + M::KW * h;
+        const T* dorow = dOb + (qb * 32 + (l & 31)) * QLD + M::KW * h;
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
-          sacc[qb] = M::mma(ld_nat(qrow + c * M::KD), kf[c], sacc[qb]);
-          pacc[qb] = M::mma(ld_nat(dorow + c * M::KD), vf[c], pacc[qb]);
+          sacc = M::mma(ld_nat(qrow + c * M::KD), kf[c], sacc);
+          pacc = M::mma(ld_nat(dorow + c * M::KD), vf[c], pacc);
         }
-      }
-
-      const bool need_mask = (q0 + BQ > S) || (jw0 + 32 > S) || (causal && jw0 + 31 > q0);
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
+        // p = 2^(s c - L log2 e), dS = p (dp - D); masked pairs give p = 0
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int r0 = qb * 32 + 8 * g + 4 * h;
-          const f32x4 L4 = *reinterpret_cast<const f32x4*>(Ls + r0);
-          const f32x4 D4 = *reinterpret_cast<const f32x4*>(Ds + r0);
+          const f32x4 L4 = *reinterpret_cast<const f32x4*>(Ls[buf] + r0);
+          const f32x4 D4 = *reinterpret_cast<const f32x4*>(Ds[buf] + r0);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int v = 4 * g + e;
-            float p = __builtin_amdgcn_exp2f(sacc[qb][v] * scale_log2 - L4[e]);
-            if (need_mask) {
-              const int q = q0 + r0 + e;
-              if (q >= S || kj >= S || (causal && kj > q)) p = 0.f;
-            }
-            sacc[qb][v] = p;
-            pacc[qb][v] = p * (pacc[qb][v] - D4[e]) * scale;
+            float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[v], c_log2, -L4[e]));
+            sacc[v] = p;
+            pacc[v] = p * (pacc[v] - D4[e]);
           }
         }
-      }
-
-      // dV^T += dO^T . P,  dK^T += Q^T . dS   (k runs over the tile's queries)
+        if (need_mask) {
+          const int base = q0 + qb * 32 + 4 * h;
+          const int lo = q_lo - base, hi = q_hi - base;
 #pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
+          for (int v = 0; v < 16; ++v) {
+            const int rel = 8 * (v >> 2) + (v & 3);
+            const bool keep = (rel >= lo) & (rel < hi);
+            sacc[v] = keep ? sacc[v] : 0.f;
+            pacc[v] = keep ? pacc[v] : 0.f;
+          }
+        }
+        // dV^T += dO^T . P,  dK^T += Q^T . dS   (k runs over the block's queries)
 #pragma unroll
         for (int u = 0; u < NU; ++u) {
-          const typename M::frag pf = frag_from_acc(sacc[qb], u, T{});
-          const typename M::frag sf = frag_from_acc(pacc[qb], u, T{});
+          const typename M::frag pf = frag_from_acc(sacc, u, T{});
+          const typename M::frag sf = frag_from_acc(pacc, u, T{});
 #pragma unroll
           for (int d = 0; d < NDB; ++d) {
-            dvacc[d] = M::mma(ld_res(dOs, QLD, qb * 32, u, d * 32), pf, dvacc[d]);
-            dkacc[d] = M::mma(ld_res(Qs, QLD, qb * 32, u, d * 32), sf, dkacc[d]);
+            dvacc[d] = M::mma(ld_res(dOb, QLD, qb * 32, u, d * 32), pf, dvacc[d]);
+            dkacc[d] = M::mma(ld_res(Qb, QLD, qb * 32, u, d * 32), sf, dkacc[d]);
           }
         }
-      }
-
-      // dS to LDS as [key][query]: 4 consecutive queries per store
-      T* srow = dSs + (32 * w + (l & 31)) * SLD;
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
+        // dS to LDS as [key][query]: 4 consecutive queries per store
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int c0 = qb * 32 + 8 * g + 4 * h;
           if constexpr (sizeof(T) == 2) {
             *reinterpret_cast<bf16x4*>(srow + c0) =
-                bf16x4{(bf16)pacc[qb][4 * g], (bf16)pacc[qb][4 * g + 1], (bf16)pacc[qb][4 * g + 2],
-                       (bf16)pacc[qb][4 * g + 3]};
+                bf16x4{(bf16)pacc[4 * g], (bf16)pacc[4 * g + 1], (bf16)pacc[4 * g + 2], (bf16)pacc[4 * g + 3]};
           } else {
             *reinterpret_cast<f32x4*>(srow + c0) =
-                f32x4{pacc[qb][4 * g], pacc[qb][4 * g + 1], pacc[qb][4 * g + 2], pacc[qb][4 * g + 3]};
+                f32x4{pacc[4 * g], pacc[4 * g + 1], pacc[4 * g + 2], pacc[4 * g + 3]};
           }
         }
-      }
-    } else {
-      T* srow = dSs + (32 * w + (l & 31)) * SLD;
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
+      } else {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int c0 = qb * 32 + 8 * g + 4 * h;
@@ -267,7 +263,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_kernel(
 #pragma unroll
     for (int ob = 0; ob < OBW; ++ob) {
       const int b = w + NW * ob;
-      if (b < NOB) {
+      if (NOB % NW == 0 || b < NOB) {
         const int qb = b / NDB, db = b - (b / NDB) * NDB;
         f32x16 acc = zero16();
         for (int kb = 0; kb < nkb; ++kb) {
@@ -276,40 +272,40 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_kernel(
             acc = M::mma(ld_res(dSs, SLD, kb * 32, u, qb * 32), ld_res(Ks, QLD, kb * 32, u, db * 32), acc);
         }
         const int d = db * 32 + (l & 31);
-        if (d < HD) {
+        if (HDP == HD || d < HD) {
+          // rows past the sequence end fall outside the buffer and are dropped
+          const uint32_t off0 = ((uint32_t)(q0 + qb * 32 + 4 * h) * HD + d) * 4u;
 #pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int q = q0 + qb * 32 + acc_row(v, h);
-            if (q < S) atomic_add_f32(dQh + (size_t)q * HD + d, acc[v]);
-          }
+          for (int v = 0; v < 16; ++v)
+            batomic_add(rAcc, off0 + (uint32_t)(8 * (v >> 2) + (v & 3)) * HD * 4u, acc[v]);
         }
       }
     }
+
+    // stage the next query tile into the other buffer while others finish dQ
+    if (qt + 1 < nqt) {
+      stage(buf ^ 1);
+      if (qt + 2 < nqt) prefetch(qt + 2);
+    }
+    __syncthreads();
   }
 
-  // dK_j, dV_j for this lane's key: C tile column = key, rows = d
-  if (kj < S) {
-    T* dkrow = dK + hoff + (size_t)kj * HD;
-    T* dvrow = dV + hoff + (size_t)kj * HD;
+  // dK_j (scaled here), dV_j for this lane's key: C tile column = key, rows = d
+  {
+    const rsrc_t rdK = make_rsrc(dK + hoff, head_bytes);
+    const rsrc_t rdV = make_rsrc(dV + hoff, head_bytes);
+    const uint32_t krow = (uint32_t)kj * ROWB;   // keys past the end are dropped
 #pragma unroll
     for (int d = 0; d < NDB; ++d) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int dd = d * 32 + 8 * g + 4 * h;
-        if (dd < HD) {
-          if constexpr (sizeof(T) == 2) {
-            *reinterpret_cast<bf16x4*>(dkrow + dd) =
-                bf16x4{(bf16)dkacc[d][4 * g], (bf16)dkacc[d][4 * g + 1], (bf16)dkacc[d][4 * g + 2],
-                       (bf16)dkacc[d][4 * g + 3]};
-            *reinterpret_cast<bf16x4*>(dvrow + dd) =
-                bf16x4{(bf16)dvacc[d][4 * g], (bf16)dvacc[d][4 * g + 1], (bf16)dvacc[d][4 * g + 2],
-                       (bf16)dvacc[d][4 * g + 3]};
-          } else {
-            *reinterpret_cast<f32x4*>(dkrow + dd) =
-                f32x4{dkacc[d][4 * g], dkacc[d][4 * g + 1], dkacc[d][4 * g + 2], dkacc[d][4 * g + 3]};
-            *reinterpret_cast<f32x4*>(dvrow + dd) =
-                f32x4{dvacc[d][4 * g], dvacc[d][4 * g + 1], dvacc[d][4 * g + 2], dvacc[d][4 * g + 3]};
-          }
+        if (HDP == HD || dd < HD) {
+          const uint32_t off = krow + dd * sizeof(T);
+          bstore_row4(rdK, off, dkacc[d][4 * g] * scale, dkacc[d][4 * g + 1] * scale,
+                      dkacc[d][4 * g + 2] * scale, dkacc[d][4 * g + 3] * scale, T{});
+          bstore_row4(rdV, off, dvacc[d][4 * g], dvacc[d][4 * g + 1], dvacc[d][4 * g + 2],
+                      dvacc[d][4 * g + 3], T{});
         }
       }
     }
@@ -321,6 +317,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_kernel(
   __threadfence();
   __syncthreads();
   unsigned* cnt = counters + (size_t)bh * nqt;
+  const rsrc_t rdQ = make_rsrc(dQ + hoff, head_bytes);
   for (int base = qt_first; base < nqt; base += NT) {
     const int qt = base + tid;
     int last = 0;
@@ -335,17 +332,12 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_kernel(
     for (int t = 0; t < nbatch; ++t) {
       if (!last_of[t]) continue;
       __threadfence();
-      const int r0 = (base + t) * BQ;
-      const int nr = min(BQ, S - r0);
-      const float* src = dQh + (size_t)r0 * HD;
-      T* dst = dQ + hoff + (size_t)r0 * HD;
-      for (int e = tid * 4; e < nr * HD; e += NT * 4) {
-        const f32x4 x = *reinterpret_cast<const f32x4*>(src + e);
-        if constexpr (sizeof(T) == 2) {
-          *reinterpret_cast<bf16x4*>(dst + e) = bf16x4{(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]};
-        } else {
-          *reinterpret_cast<f32x4*>(dst + e) = x;
-        }
+      const uint32_t e0 = (uint32_t)(base + t) * BQ * HD;   // first element of the tile
+      const int n = min(BQ, S - (base + t) * BQ) * HD;
+      for (int e = tid * 4; e < n; e += NT * 4) {
+        const f32x4 x = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                      rAcc, (e0 + e) * 4u, 0, 0));
+        bstore_row4(rdQ, (e0 + e) * sizeof(T), x[0] * scale, x[1] * scale, x[2] * scale, x[3] * scale, T{});
       }
     }
     __syncthreads();
@@ -355,8 +347,8 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_kernel(
 template <typename T, int HD>
 struct BwdCfg {
   static constexpr int NW = 4;
-  // fp32 tiles at hd = 128 would not fit the 160 KiB of LDS with 64 queries
-  static constexpr int BQ = (sizeof(T) == 4 && HD == 128) ? 32 : 64;
+  // fp32 tiles at hd >= 64 would not fit the 160 KiB of LDS with 64 queries
+  static constexpr int BQ = (sizeof(T) == 4 && HD >= 64) ? 32 : 64;
 };
 
 template <typename T, int HD>
@@ -375,7 +367,12 @@ static hipError_t launch_bwd_t(const BwdArgs& a) {
 
 int bwd_query_tile(bool is_bf16, int64_t hd) {
   if (is_bf16) return BwdCfg<bf16, 64>::BQ;
-  return hd == 128 ? BwdCfg<float, 128>::BQ : BwdCfg<float, 64>::BQ;
+  switch (hd) {
+    case 16: return BwdCfg<float, 16>::BQ;
+    case 32: return BwdCfg<float, 32>::BQ;
+    case 64: return BwdCfg<float, 64>::BQ;
+  }
+  return BwdCfg<float, 128>::BQ;
 }
 
 size_t bwd_workspace(void* base, int64_t BH, int64_t S, int64_t hd, bool is_bf16, Workspace* ws) {

@@ -128,6 +128,44 @@ __device__ inline void st16(T* p, const typename Vec16<T>::type& v) {
   *reinterpret_cast<typename Vec16<T>::type*>(p) = v;
 }
 
+// ------------------------------------------------ buffer-resource access
+// Global memory is addressed through buffer resources: a uniform base and
+// size in scalar registers plus a 32-bit per-lane byte offset.  Loads past
+// the end return zeros and stores past the end are dropped by the hardware,
+// which handles ragged sequence tails without branches.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+constexpr int kRsrcWord3 = 0x00020000;   // raw (unformatted) 32-bit data
+
+__device__ inline rsrc_t make_rsrc(const void* base, uint32_t nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nbytes, kRsrcWord3);
+}
+template <typename T>
+__device__ inline typename Vec16<T>::type bload16(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(typename Vec16<T>::type, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ inline float bload4(rsrc_t r, uint32_t off) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+__device__ inline void bstore16(rsrc_t r, uint32_t off, u32x4 v) { __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0); }
+__device__ inline void bstore8(rsrc_t r, uint32_t off, u32x2 v) { __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, 0); }
+__device__ inline void bstore4(rsrc_t r, uint32_t off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);
+}
+__device__ inline void batomic_add(rsrc_t r, uint32_t off, float v) {
+  __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(v, r, off, 0, 0);
+}
+
+// Four consecutive results of a C tile as an 8-byte (bf16) or 16-byte (fp32) store.
+__device__ inline void bstore_row4(rsrc_t r, uint32_t off, float a, float b, float c, float d, bf16) {
+  bf16x4 x{(bf16)a, (bf16)b, (bf16)c, (bf16)d};
+  bstore8(r, off, __builtin_bit_cast(u32x2, x));
+}
+__device__ inline void bstore_row4(rsrc_t r, uint32_t off, float a, float b, float c, float d, float) {
+  bstore16(r, off, u32x4{__float_as_uint(a), __float_as_uint(b), __float_as_uint(c), __float_as_uint(d)});
+}
+
 // Workgroup order for 8 XCDs: the hardware hands consecutive workgroup ids to
 // the XCDs in turn.  Remap so that each XCD walks a contiguous range of the
 // logical order (keeping one head's workgroups, which share K/V or Q/dO, in

@@ -13,7 +13,9 @@
 // registers as the B operand; V^T is read from the row-major V tile with the
 // LDS transpose read.  K and V tiles are staged in LDS, with the next tile's
 // global loads in flight while the current one is processed.  The exponent is
-// taken in base 2 with log2(e) folded into the score scale.
+// taken in base 2: with c = scale * log2(e) and m the running maximum of the
+// raw logits, p = 2^(x c - m c) is one fused multiply-add and one exp2.
+// Only tiles that cross the diagonal or the sequence end evaluate the mask.
 #include "xfa_common.h"
 #include "xfa_launch.h"
 
@@ -22,7 +24,7 @@ namespace xfa {
 template <typename T, int HD, int NW, int BK>
 __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, T* __restrict__ O,
-    float* __restrict__ Lse, int S, float scale_log2, int causal, int nqt, int nwg) {
+    float* __restrict__ Lse, int S, float c_log2, int causal, int nqt, int nwg) {
   using M = Mma<T>;
   constexpr int BQ = NW * 32;
   constexpr int NT = NW * 64;
@@ -37,6 +39,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(
   constexpr int VLD = HDP + (sizeof(T) == 2 ? 16 : 4);
   constexpr int TILE_CHUNKS = BK * CPR;
   constexpr int PF = (TILE_CHUNKS + NT - 1) / NT;       // chunks per thread per tile
+  constexpr uint32_t ROWB = HD * sizeof(T);             // bytes per row in HBM
   static_assert(HD % M::KD == 0 && HD % VE == 0, "unsupported head dim");
 
   __shared__ __attribute__((aligned(16))) T Ks[BK * KLD];
@@ -53,9 +56,10 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(
   const int qt = nqt - 1 - (lid - bh * nqt);
 
   const size_t hoff = (size_t)bh * S * HD;
-  const T* Qh = Q + hoff;
-  const T* Kh = K + hoff;
-  const T* Vh = V + hoff;
+  const uint32_t head_bytes = (uint32_t)S * ROWB;
+  const rsrc_t rQ = make_rsrc(Q + hoff, head_bytes);
+  const rsrc_t rK = make_rsrc(K + hoff, head_bytes);
+  const rsrc_t rV = make_rsrc(V + hoff, head_bytes);
 
   const int q0 = qt * BQ;
   const int qw0 = q0 + 32 * w;                   // first query of this wave
@@ -64,6 +68,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(
   const int qw_last = min(qw0 + 31, S - 1);      // last real query of this wave
   const bool wave_live = qw0 < S;
   const int n_tiles = causal ? (q_last / BK + 1) : ((S + BK - 1) / BK);
+  // last key this lane's query may see
+  const int key_lim = causal ? min(qi, S - 1) : S - 1;
 
   // padding columns of the V tile (d >= HD) stay zero for the whole kernel
   if constexpr (HDP != HD) {
@@ -77,8 +83,9 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(
   typename M::frag qf[NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
-    if (qi < S) qf[c] = ld_nat(Qh + (size_t)qi * HD + c * M::KD + M::KW * h);
-    else qf[c] = M::zero();
+    const uint32_t off = (uint32_t)qi * ROWB + (c * M::KD + M::KW * h) * sizeof(T);
+    if constexpr (sizeof(T) == 2) qf[c] = bload16<bf16>(rQ, off);
+    else qf[c] = bload4(rQ, off);
   }
 
   typename Vec16<T>::type pk[PF], pv[PF];
@@ -87,13 +94,10 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(
     for (int i = 0; i < PF; ++i) {
       const int e = tid + i * NT;
       const int r = e / CPR, c = (e - r * CPR) * VE;
-      const int key = kt * BK + r;
-      if (e < TILE_CHUNKS && key < S) {
-        pk[i] = ld16(Kh + (size_t)key * HD + c);
-        pv[i] = ld16(Vh + (size_t)key * HD + c);
-      } else {
-        pk[i] = typename Vec16<T>::type{};
-        pv[i] = typename Vec16<T>::type{};
+      const uint32_t off = (uint32_t)(kt * BK + r) * ROWB + c * sizeof(T);
+      if (TILE_CHUNKS % NT == 0 || e < TILE_CHUNKS) {
+        pk[i] = bload16<T>(rK, off);   // rows past the end read as zeros
+        pv[i] = bload16<T>(rV, off);
       }
     }
   };
@@ -101,7 +105,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(
 #pragma unroll
     for (int i = 0; i < PF; ++i) {
       const int e = tid + i * NT;
-      if (e < TILE_CHUNKS) {
+      if (TILE_CHUNKS % NT == 0 || e < TILE_CHUNKS) {
         const int r = e / CPR, c = (e - r * CPR) * VE;
         st16(Ks + r * KLD + c, pk[i]);
         st16(Vs + r * VLD + c, pv[i]);
@@ -112,7 +116,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(
   f32x16 oacc[NDB];
 #pragma unroll
   for (int d = 0; d < NDB; ++d) oacc[d] = zero16();
-  float m_run = kNegInf;   // running max of this lane's query, log2 units
+  float m_run = kNegInf;   // running max of this lane's raw logits
   float l_run = 0.f;       // running sum over the keys this lane half holds
 
   prefetch(0);
@@ -135,32 +139,34 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(
       for (int c = 0; c < NC; ++c) sacc[kb] = M::mma(ld_nat(krow + c * M::KD), qf[c], sacc[kb]);
     }
 
-    const bool need_mask = (k0 + BK > S) || (causal && k0 + BK - 1 > qw0);
-    float mt = kNegInf;
+    // mask keys past this query (causal) or past the sequence end; only tiles
+    // that reach the diagonal or the end need it
+    if ((k0 + BK > S) || (causal && k0 + BK - 1 > qw0)) {
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
+      for (int kb = 0; kb < NKB; ++kb) {
+        const int rel = key_lim - (k0 + kb * 32 + 4 * h);
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        float s = sacc[kb][v] * scale_log2;
-        if (need_mask) {
-          const int key = k0 + kb * 32 + acc_row(v, h);
-          if (key >= S || (causal && key > qi)) s = kNegInf;
-        }
-        sacc[kb][v] = s;
-        mt = fmaxf(mt, s);
+        for (int v = 0; v < 16; ++v)
+          sacc[kb][v] = (8 * (v >> 2) + (v & 3) > rel) ? kNegInf : sacc[kb][v];
       }
     }
+    float mt = kNegInf;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) mt = fmaxf(mt, sacc[kb][v]);
     mt = fmaxf(mt, swap_halves(mt));
     const float m_new = fmaxf(m_run, mt);   // finite: key 0 is visible to every query
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c_log2);
     m_run = m_new;
+    const float mc = m_new * c_log2;
 
     float ps = 0.f;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const float p = __builtin_amdgcn_exp2f(sacc[kb][v] - m_new);
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][v], c_log2, -mc));
         sacc[kb][v] = p;
         ps += p;
       }
@@ -184,27 +190,22 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(
   if (!wave_live) return;
   const float l_tot = l_run + swap_halves(l_run);
   const float inv_l = 1.f / l_tot;
-  if (qi < S) {
-    T* orow = O + hoff + (size_t)qi * HD;
+  // rows past the sequence end fall outside the buffer and are dropped
+  const rsrc_t rO = make_rsrc(O + hoff, head_bytes);
+  const uint32_t orow = (uint32_t)qi * ROWB;
 #pragma unroll
-    for (int d = 0; d < NDB; ++d) {
+  for (int d = 0; d < NDB; ++d) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int dd = d * 32 + 8 * g + 4 * h;
-        if (dd < HD) {
-          if constexpr (sizeof(T) == 2) {
-            bf16x4 o4{(bf16)(oacc[d][4 * g + 0] * inv_l), (bf16)(oacc[d][4 * g + 1] * inv_l),
-                      (bf16)(oacc[d][4 * g + 2] * inv_l), (bf16)(oacc[d][4 * g + 3] * inv_l)};
-            *reinterpret_cast<bf16x4*>(orow + dd) = o4;
-          } else {
-            f32x4 o4{oacc[d][4 * g + 0] * inv_l, oacc[d][4 * g + 1] * inv_l,
-                     oacc[d][4 * g + 2] * inv_l, oacc[d][4 * g + 3] * inv_l};
-            *reinterpret_cast<f32x4*>(orow + dd) = o4;
-          }
-        }
-      }
+    for (int g = 0; g < 4; ++g) {
+      const int dd = d * 32 + 8 * g + 4 * h;
+      if (HDP == HD || dd < HD)
+        bstore_row4(rO, orow + dd * sizeof(T), oacc[d][4 * g] * inv_l, oacc[d][4 * g + 1] * inv_l,
+                    oacc[d][4 * g + 2] * inv_l, oacc[d][4 * g + 3] * inv_l, T{});
     }
-    if (h == 0) Lse[(size_t)bh * S + qi] = (m_run + __log2f(l_tot)) * kLn2;
+  }
+  if (h == 0) {
+    const rsrc_t rL = make_rsrc(Lse + (size_t)bh * S, (uint32_t)S * 4u);
+    bstore4(rL, (uint32_t)qi * 4u, (m_run * c_log2 + __log2f(l_tot)) * kLn2);
   }
 }
 
@@ -214,12 +215,10 @@ static hipError_t launch_fwd_t(const FwdArgs& a) {
   constexpr int BK = 64;
   constexpr int BQ = NW * 32;
   const int nqt = (int)((a.S + BQ - 1) / BQ);
-  const long long nwg_ll = (long long)a.BH * nqt;
-  const int nwg = (int)nwg_ll;
-  const float scale_log2 = a.scale * kLog2e;
+  const int nwg = (int)(a.BH * nqt);
   hipLaunchKernelGGL((fwd_kernel<T, HD, NW, BK>), dim3(nwg), dim3(NW * 64), 0, a.stream,
                      (const T*)a.q, (const T*)a.k, (const T*)a.v, (T*)a.out, a.lse, (int)a.S,
-                     scale_log2, a.causal, nqt, nwg);
+                     a.scale * kLog2e, a.causal, nqt, nwg);
   return hipGetLastError();
 }
 
