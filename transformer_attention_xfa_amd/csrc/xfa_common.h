@@ -166,6 +166,43 @@ __device__ inline void bstore_row4(rsrc_t r, uint32_t off, float a, float b, flo
   bstore16(r, off, u32x4{__float_as_uint(a), __float_as_uint(b), __float_as_uint(c), __float_as_uint(d)});
 }
 
+// ------------------------------------------------ transposed bf16 tiles
+// Operands whose contraction index runs along the rows of a row-major tile
+// (V for P.V, Q and dO for the dK / dV sums, K for dQ) are kept in LDS
+// transposed: T[c][pos] holds X[row][c] for the tile's R rows, so that an
+// operand fragment (8 k-values of one column) is a single 16-byte read.  The
+// fragment a result-order operand needs (rows 8a + 4h + b of a 16-row group
+// for slot 4a + b of lane half h) becomes contiguous by storing row r at
+// position swap23(r) (bits 2 and 3 of r exchanged).  Each T row holds R/8
+// 16-byte chunks; chunks are XOR-swizzled by the row index so that 16
+// consecutive T rows read at the same logical chunk hit distinct banks.
+//
+// Staging: a unit is a 4-row x 2-column block loaded with four 4-byte loads
+// (rows r..r+3, columns c, c+1); two byte permutes make the 4-row groups of
+// column c and column c+1, each written as 8 bytes.  Lanes whose index has
+// bit 3 set write column c+1 first, which spreads each write across both
+// halves of the banks.
+template <int R>
+struct TTile {
+  static constexpr int NCH = R / 8;                       // 16-byte chunks per T row
+  static constexpr int RPB = R >= 128 ? 1 : 128 / R;      // T rows per 256-byte bank sweep
+  static constexpr int ROWW = R / 2;                      // dwords per T row
+  __device__ static inline int sw(int c) { return (c / RPB) & (NCH - 1); }
+  // dword address of the chunk holding positions 8j..8j+7 of T row c
+  __device__ static inline int chunk_dw(int c, int j) { return c * ROWW + 4 * (j ^ sw(c)); }
+};
+
+__device__ inline int swap23(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
+
+// Four rows x two bf16 columns (as loaded) -> the 4-row groups of each column.
+__device__ inline void transpose_4x2(const unsigned x[4], u32x2& col0, u32x2& col1) {
+  // v_perm_b32(a, b, sel): byte k of the result is byte sel[k] of {a (bytes 4..7), b (bytes 0..3)}
+  col0[0] = __builtin_amdgcn_perm(x[1], x[0], 0x05040100u);   // r0.c0, r1.c0
+  col0[1] = __builtin_amdgcn_perm(x[3], x[2], 0x05040100u);   // r2.c0, r3.c0
+  col1[0] = __builtin_amdgcn_perm(x[1], x[0], 0x07060302u);   // r0.c1, r1.c1
+  col1[1] = __builtin_amdgcn_perm(x[3], x[2], 0x07060302u);   // r2.c1, r3.c1
+}
+
 // Workgroup order for 8 XCDs: the hardware hands consecutive workgroup ids to
 // the XCDs in turn.  Remap so that each XCD walks a contiguous range of the
 // logical order (keeping one head's workgroups, which share K/V or Q/dO, in

@@ -10,12 +10,16 @@
 // row max / row sum of the online softmax are then in-lane reductions plus one
 // exchange between the two lane halves, and the per-query rescale factor is a
 // per-lane scalar.  O^T = V^T . P^T reuses the score tile straight from
-// registers as the B operand; V^T is read from the row-major V tile with the
-// LDS transpose read.  K and V tiles are staged in LDS, with the next tile's
+// registers as the B operand; for bf16 the V tile is staged into LDS already
+// transposed (a swizzled [d][key] layout, see TTile), so each V^T fragment is
+// one 16-byte read.  K and V tiles are staged in LDS, with the next tile's
 // global loads in flight while the current one is processed.  The exponent is
-// taken in base 2: with c = scale * log2(e) and m the running maximum of the
-// raw logits, p = 2^(x c - m c) is one fused multiply-add and one exp2.
-// Only tiles that cross the diagonal or the sequence end evaluate the mask.
+// taken in base 2: with c = scale * log2(e) and a reference maximum m (log2
+// units), p = 2^(x c - m) is one fused multiply-add and one exp2.  Only tiles
+// that cross the diagonal or the sequence end evaluate the mask, and the row
+// sum l is taken over the bf16-rounded weights that enter P.V.
+#include <type_traits>
+
 #include "xfa_common.h"
 #include "xfa_launch.h"
 
@@ -42,8 +46,14 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(
   constexpr uint32_t ROWB = HD * sizeof(T);             // bytes per row in HBM
   static_assert(HD % M::KD == 0 && HD % VE == 0, "unsupported head dim");
 
+  constexpr bool TV = sizeof(T) == 2;           // bf16: V staged transposed
+  using TT = TTile<BK>;
+  constexpr int VUN = (BK / 4) * (HD / 2);      // 4-row x 2-column units of a V tile
+  constexpr int PFV = TV ? (VUN + NT - 1) / NT : PF;
+  constexpr int VS_ELEMS = TV ? HDP * BK : BK * VLD;
+
   __shared__ __attribute__((aligned(16))) T Ks[BK * KLD];
-  __shared__ __attribute__((aligned(16))) T Vs[BK * VLD];
+  __shared__ __attribute__((aligned(16))) T Vs[VS_ELEMS];
 
   const int tid = threadIdx.x;
   const int l = lane();
@@ -71,11 +81,15 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(
   // last key this lane's query may see
   const int key_lim = causal ? min(qi, S - 1) : S - 1;
 
-  // padding columns of the V tile (d >= HD) stay zero for the whole kernel
+  // padding of the V tile (d >= HD) stays zero for the whole kernel
   if constexpr (HDP != HD) {
-    for (int e = tid; e < BK * (HDP - HD); e += NT) {
-      const int r = e / (HDP - HD), c = HD + e % (HDP - HD);
-      Vs[r * VLD + c] = (T)0.f;
+    if constexpr (TV) {
+      for (int e = tid; e < (HDP - HD) * BK; e += NT) Vs[HD * BK + e] = (T)0.f;
+    } else {
+      for (int e = tid; e < BK * (HDP - HD); e += NT) {
+        const int r = e / (HDP - HD), c = HD + e % (HDP - HD);
+        Vs[r * VLD + c] = (T)0.f;
+      }
     }
   }
 
@@ -88,7 +102,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(
     else qf[c] = bload4(rQ, off);
   }
 
-  typename Vec16<T>::type pk[PF], pv[PF];
+  typename Vec16<T>::type pk[PF], pv[TV ? 1 : PF];
+  unsigned pvt[TV ? PFV : 1][4];
   auto prefetch = [&](int kt) {
 #pragma unroll
     for (int i = 0; i < PF; ++i) {
@@ -97,7 +112,19 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(
       const uint32_t off = (uint32_t)(kt * BK + r) * ROWB + c * sizeof(T);
       if (TILE_CHUNKS % NT == 0 || e < TILE_CHUNKS) {
         pk[i] = bload16<T>(rK, off);   // rows past the end read as zeros
-        pv[i] = bload16<T>(rV, off);
+        if constexpr (!TV) pv[i] = bload16<T>(rV, off);
+      }
+    }
+    if constexpr (TV) {
+#pragma unroll
+      for (int i = 0; i < PFV; ++i) {
+        const int e = tid + i * NT;
+        const int cp = e % (HD / 2), rg = e / (HD / 2);
+        const uint32_t off = (uint32_t)(kt * BK + 4 * rg) * ROWB + cp * 4u;
+        if (VUN % NT == 0 || e < VUN) {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) pvt[i][k] = __float_as_uint(bload4(rV, off + k * ROWB));
+        }
       }
     }
   };
@@ -108,7 +135,25 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(
       if (TILE_CHUNKS % NT == 0 || e < TILE_CHUNKS) {
         const int r = e / CPR, c = (e - r * CPR) * VE;
         st16(Ks + r * KLD + c, pk[i]);
-        st16(Vs + r * VLD + c, pv[i]);
+        if constexpr (!TV) st16(Vs + r * VLD + c, pv[i]);
+      }
+    }
+    if constexpr (TV) {
+      unsigned* vt = reinterpret_cast<unsigned*>(Vs);
+#pragma unroll
+      for (int i = 0; i < PFV; ++i) {
+        const int e = tid + i * NT;
+        if (VUN % NT == 0 || e < VUN) {
+          const int cp = e % (HD / 2), rg = e / (HD / 2);
+          const int p = swap23(4 * rg);
+          u32x2 col0, col1;
+          transpose_4x2(pvt[i], col0, col1);
+          const bool odd_first = (l >> 3) & 1;
+          const int c_first = 2 * cp + (odd_first ? 1 : 0);
+          const int dw_half = 2 * ((p >> 2) & 1);
+          *reinterpret_cast<u32x2*>(vt + TT::chunk_dw(c_first, p >> 3) + dw_half) = odd_first ? col1 : col0;
+          *reinterpret_cast<u32x2*>(vt + TT::chunk_dw(c_first ^ 1, p >> 3) + dw_half) = odd_first ? col0 : col1;
+        }
       }
     }
   };
@@ -116,20 +161,15 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(
   f32x16 oacc[NDB];
 #pragma unroll
   for (int d = 0; d < NDB; ++d) oacc[d] = zero16();
-  float m_run = kNegInf;   // running max of this lane's raw logits
+  // The reference maximum m_ref (log2 units) only moves when some lane's
+  // tile maximum exceeds it by more than kRescale; until then p stays below
+  // 2^kRescale and the accumulators need no rescaling.  out = acc / l does
+  // not depend on the reference, so this changes no result beyond rounding.
+  constexpr float kRescale = 8.f;
+  float m_ref = kNegInf;
   float l_run = 0.f;       // running sum over the keys this lane half holds
 
-  prefetch(0);
-  for (int kt = 0; kt < n_tiles; ++kt) {
-    __syncthreads();
-    stage();
-    __syncthreads();
-    if (kt + 1 < n_tiles) prefetch(kt + 1);
-
-    const int k0 = kt * BK;
-    // the wave skips tiles wholly above its part of the diagonal
-    if (!wave_live || (causal && k0 > qw_last)) continue;
-
+  auto tile = [&](auto masked, int k0) {
     f32x16 sacc[NKB];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
@@ -138,10 +178,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(
 #pragma unroll
       for (int c = 0; c < NC; ++c) sacc[kb] = M::mma(ld_nat(krow + c * M::KD), qf[c], sacc[kb]);
     }
-
-    // mask keys past this query (causal) or past the sequence end; only tiles
-    // that reach the diagonal or the end need it
-    if ((k0 + BK > S) || (causal && k0 + BK - 1 > qw0)) {
+    if constexpr (decltype(masked)::value) {
+      // keys past this query (causal) or past the sequence end
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
         const int rel = key_lim - (k0 + kb * 32 + 4 * h);
@@ -155,37 +193,66 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) mt = fmaxf(mt, sacc[kb][v]);
-    mt = fmaxf(mt, swap_halves(mt));
-    const float m_new = fmaxf(m_run, mt);   // finite: key 0 is visible to every query
-    const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c_log2);
-    m_run = m_new;
-    const float mc = m_new * c_log2;
-
-    float ps = 0.f;
+    mt = fmaxf(mt, swap_halves(mt)) * c_log2;   // row maximum, log2 units (scale > 0)
+    if (__builtin_amdgcn_ballot_w64(mt > m_ref + kRescale)) {
+      const float m_new = fmaxf(m_ref, mt);     // key 0 is visible to every query
+      const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
+      m_ref = m_new;
+      l_run *= alpha;
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][v], c_log2, -mc));
-        sacc[kb][v] = p;
-        ps += p;
-      }
+      for (int d = 0; d < NDB; ++d) oacc[d] *= alpha;
     }
-    l_run = l_run * alpha + ps;
 #pragma unroll
-    for (int d = 0; d < NDB; ++d) oacc[d] *= alpha;
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        sacc[kb][v] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][v], c_log2, -m_ref));
 
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
       for (int u = 0; u < NU; ++u) {
         const typename M::frag pf = frag_from_acc(sacc[kb], u, T{});
+        if constexpr (sizeof(T) == 2) {
+          // row sum of the bf16 weights that enter P.V, two per dot2
+          typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+          const bf16x2 one2{(bf16)1.f, (bf16)1.f};
 #pragma unroll
-        for (int d = 0; d < NDB; ++d)
-          oacc[d] = M::mma(ld_res(Vs, VLD, kb * 32, u, d * 32), pf, oacc[d]);
+          for (int e = 0; e < 4; ++e)
+            l_run = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[2 * e], pf[2 * e + 1]}, one2, l_run, false);
+        } else {
+          l_run += pf;
+        }
+#pragma unroll
+        for (int d = 0; d < NDB; ++d) {
+          typename M::frag vf;
+          if constexpr (TV) {
+            const int c = d * 32 + (l & 31);
+            vf = *reinterpret_cast<const bf16x8*>(Vs + 2 * TT::chunk_dw(c, 4 * kb + 2 * u + h));
+          } else {
+            vf = ld_res(Vs, VLD, kb * 32, u, d * 32);
+          }
+          oacc[d] = M::mma(vf, pf, oacc[d]);
+        }
       }
     }
-  }
+  };
+
+  // Tiles before n_full are unmasked for every wave of the workgroup; the
+  // rest (the diagonal and the sequence end) go through the masked variant.
+  const int n_full = min(causal ? (q0 + 1) / BK : n_tiles, S / BK);
+  auto step = [&](auto masked, int kt) {
+    __syncthreads();
+    stage();
+    __syncthreads();
+    if (kt + 1 < n_tiles) prefetch(kt + 1);
+    const int k0 = kt * BK;
+    // the wave skips tiles wholly above its part of the diagonal
+    if (wave_live && !(causal && k0 > qw_last)) tile(masked, k0);
+  };
+  prefetch(0);
+  for (int kt = 0; kt < n_full; ++kt) step(std::false_type{}, kt);
+  for (int kt = n_full; kt < n_tiles; ++kt) step(std::true_type{}, kt);
 
   if (!wave_live) return;
   const float l_tot = l_run + swap_halves(l_run);
@@ -205,7 +272,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(
   }
   if (h == 0) {
     const rsrc_t rL = make_rsrc(Lse + (size_t)bh * S, (uint32_t)S * 4u);
-    bstore4(rL, (uint32_t)qi * 4u, (m_run * c_log2 + __log2f(l_tot)) * kLn2);
+    bstore4(rL, (uint32_t)qi * 4u, (m_ref + __log2f(l_tot)) * kLn2);
   }
 }
 
