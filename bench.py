@@ -80,7 +80,6 @@ def gpu_bench(x, steps: int, warmup: int):
     lse = torch.empty((B, H, S), dtype=torch.float32, device=dev)
     delta = torch.empty_like(lse)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
-    ws = xfa.workspace_for(q)
     scale, causal = w.sm_scale, w.causal
     stream = torch.cuda.current_stream()
 
@@ -90,10 +89,10 @@ def gpu_bench(x, steps: int, warmup: int):
         xfa.xfa_fwd(q, k, v, out, lse, scale, causal, stream)
         if ev is not None:
             ev[1].record(stream)
-        xfa.xfa_bwd_preprocess(out, do, delta, ws, scale, causal, stream)
+        xfa.xfa_bwd_preprocess(out, do, delta, scale, causal, stream)
         if ev is not None:
             ev[2].record(stream)
-        xfa.xfa_bwd(q, k, v, do, lse, delta, dq, dk, dv, ws, scale, causal, stream)
+        xfa.xfa_bwd(q, k, v, do, lse, delta, dq, dk, dv, scale, causal, stream)
         if ev is not None:
             ev[3].record(stream)
 
@@ -181,7 +180,7 @@ def main(argv=None):
         "avg_launch_ms": round(ms_mean[dom], 4),
     }
     el = 2 if w.dtype == "bf16" else 4
-    pre_bytes = w.BH * w.S * (2 * w.hd * el + 4 + w.hd * 4)   # read O, dO; write D, clear dQ acc
+    pre_bytes = w.BH * w.S * (2 * w.hd * el + 4)   # read O, dO; write D
     phases = {
         "fwd": {"kernel": KERNEL_NAME["fwd"], "avg_ms": round(ms_mean["fwd"], 4), "median_ms": round(ms_med["fwd"], 4),
                 "tflops": round(w.fwd_flop / (ms_mean["fwd"] * 1e-3) / 1e12, 2)},

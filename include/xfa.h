@@ -59,7 +59,7 @@ typedef enum {
 typedef enum {
   XFA_OK = 0,
   XFA_ERR_INVALID_ARGUMENT = 1, /* null or misaligned pointer, negative size, bad scale/causal/dtype */
-  XFA_ERR_UNSUPPORTED = 2,      /* hd not in {16,32,64,128}, or sizes beyond the kernels' index range */
+  XFA_ERR_UNSUPPORTED = 2,      /* hd not in {16,32,64,128}, S > 2^30, S*hd*4 >= 2^31, or too many workgroups */
   XFA_ERR_HIP = 3               /* a kernel launch failed */
 } xfa_status_t;
 
@@ -77,20 +77,11 @@ xfa_status_t xfa_fwd(const void* q, const void* k, const void* v, void* out, flo
  * sum_d dO_i[d] * O_i[d], one O(N) pass before the backward).
  *   in : out, dout [B,H,S,hd] dtype (out as returned by xfa_fwd)
  *   out: delta     [B,H,S] float32
- *        workspace xfa_bwd_workspace_bytes(...) bytes of device memory,
- *                  16-byte aligned, cleared here for the xfa_bwd call that
- *                  follows on the same stream (pass that call the same
- *                  workspace, with no other use of it in between)
  * scale and causal do not enter D; they are checked like everywhere else so
  * that the three calls share one argument tail.                              */
-xfa_status_t xfa_bwd_preprocess(const void* out, const void* dout, float* delta, void* workspace,
+xfa_status_t xfa_bwd_preprocess(const void* out, const void* dout, float* delta,
                                 int64_t B, int64_t H, int64_t S, int64_t hd, float scale,
                                 int causal, int dtype, void* stream);
-
-/* Bytes of device workspace the backward needs for these sizes: an fp32 dQ
- * accumulator of B*H*S*hd elements plus one counter per (head, 64-query
- * tile).  Returns 0 for invalid or empty sizes.                              */
-size_t xfa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t S, int64_t hd, int dtype);
 
 /* Backward (T14 design doc, "What flash-attention is", backward part:
  * p = exp(s - L), dp = dO . V, ds = p (dp - D) scale; dQ += ds K,
@@ -98,15 +89,12 @@ size_t xfa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t S, int64_t hd, int 
  *   in : q, k, v, dout [B,H,S,hd] dtype; lse [B,H,S] from xfa_fwd;
  *        delta [B,H,S] from xfa_bwd_preprocess
  *   out: dq, dk, dv    [B,H,S,hd] dtype (fully overwritten)
- *   workspace: the workspace the preceding xfa_bwd_preprocess call cleared;
- *        on return its contents are undefined (clear it again, by calling
- *        xfa_bwd_preprocess, before the next xfa_bwd).
- * One kernel.  dQ is summed with float32 atomic adds, so its rounding can
- * differ between runs; dK and dV are deterministic.                          */
+ * One kernel, no scratch memory.  Each output element is produced by exactly
+ * one workgroup (no atomics), so results are bitwise reproducible.           */
 xfa_status_t xfa_bwd(const void* q, const void* k, const void* v, const void* dout,
                      const float* lse, const float* delta, void* dq, void* dk, void* dv,
-                     void* workspace, int64_t B, int64_t H, int64_t S, int64_t hd, float scale,
-                     int causal, int dtype, void* stream);
+                     int64_t B, int64_t H, int64_t S, int64_t hd, float scale, int causal,
+                     int dtype, void* stream);
 
 /* Static, NUL-terminated description of a status code.                       */
 const char* xfa_status_string(xfa_status_t status);

@@ -60,15 +60,14 @@ def run_gpu(x, stream=None):
     lse = torch.empty((B, H, S), dtype=torch.float32, device="cuda")
     delta = torch.empty_like(lse)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
-    ws = xfa.workspace_for(q)
     ctx = torch.cuda.stream(stream) if stream is not None else torch.cuda.stream(torch.cuda.current_stream())
     with ctx:
         xfa.xfa_fwd(q, k, v, out, lse, w.sm_scale, w.causal)
-        xfa.xfa_bwd_preprocess(out, do, delta, ws, w.sm_scale, w.causal)
-        xfa.xfa_bwd(q, k, v, do, lse, delta, dq, dk, dv, ws, w.sm_scale, w.causal)
+        xfa.xfa_bwd_preprocess(out, do, delta, w.sm_scale, w.causal)
+        xfa.xfa_bwd(q, k, v, do, lse, delta, dq, dk, dv, w.sm_scale, w.causal)
     torch.cuda.synchronize()
     res = {n: host(t) for n, t in dict(out=out, lse=lse, delta=delta, dq=dq, dk=dk, dv=dv).items()}
-    del q, k, v, do, out, lse, delta, dq, dk, dv, ws
+    del q, k, v, do, out, lse, delta, dq, dk, dv
     torch.cuda.empty_cache()
     return res
 
@@ -243,11 +242,9 @@ def test_nondefault_stream_and_repeatability():
     g0 = run_gpu(x)
     s = torch.cuda.Stream()
     g1 = run_gpu(x, stream=s)
-    for n in ("out", "lse", "delta", "dk", "dv"):
+    # every output element is produced by one workgroup: bitwise reproducible
+    for n in ("out", "lse", "delta", "dq", "dk", "dv"):
         np.testing.assert_array_equal(g0[n], g1[n], err_msg=n)
-    # dQ is summed with atomics: the order may change its rounding
-    diff = np.abs(g0["dq"] - g1["dq"]).max()
-    say(f"dq run-to-run max difference {diff:.3g}")
     for bh in range(w.BH):
         compare_head(x, g1, bh)
 

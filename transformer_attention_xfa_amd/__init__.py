@@ -16,10 +16,8 @@ from ._binding import (  # noqa: F401
     backward,
     forward,
     lib,
-    workspace_for,
     xfa_bwd,
     xfa_bwd_preprocess,
-    xfa_bwd_workspace_bytes,
     xfa_fwd,
     xfa_status_string,
 )

@@ -24,9 +24,8 @@ XFA_ERR_HIP = 3
 _c_void_p, _i64, _f32, _int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int
 _SIGS = {
     "xfa_fwd": (_int, [_c_void_p] * 5 + [_i64] * 4 + [_f32, _int, _int, _c_void_p]),
-    "xfa_bwd_preprocess": (_int, [_c_void_p] * 4 + [_i64] * 4 + [_f32, _int, _int, _c_void_p]),
-    "xfa_bwd_workspace_bytes": (ctypes.c_size_t, [_i64] * 4 + [_int]),
-    "xfa_bwd": (_int, [_c_void_p] * 10 + [_i64] * 4 + [_f32, _int, _int, _c_void_p]),
+    "xfa_bwd_preprocess": (_int, [_c_void_p] * 3 + [_i64] * 4 + [_f32, _int, _int, _c_void_p]),
+    "xfa_bwd": (_int, [_c_void_p] * 9 + [_i64] * 4 + [_f32, _int, _int, _c_void_p]),
     "xfa_status_string": (ctypes.c_char_p, [_int]),
 }
 
@@ -117,63 +116,30 @@ def xfa_fwd(q, k, v, out, lse, scale=None, causal=True, stream=None) -> None:
     _raise(st, "xfa_fwd")
 
 
-def xfa_bwd_preprocess(out, dout, delta, workspace, scale=None, causal=True, stream=None) -> None:
-    """delta [B,H,S] float32 <- rowsum(dout * out); also clears ``workspace``
-    (a GPU tensor of at least xfa_bwd_workspace_bytes bytes) for xfa_bwd."""
+def xfa_bwd_preprocess(out, dout, delta, scale=None, causal=True, stream=None) -> None:
+    """delta [B,H,S] float32 <- rowsum(dout * out)."""
     torch = _torch()
     B, H, S, hd = out.shape
     _check_same(out, out, dout, shape=out.shape, dtype=out.dtype, names=("out", "dout"))
     _check_same(out, delta, shape=(B, H, S), dtype=torch.float32, names=("delta",))
-    _check_workspace(out, workspace)
-    st = lib().xfa_bwd_preprocess(out.data_ptr(), dout.data_ptr(), delta.data_ptr(),
-                                  _ptr(workspace), B, H, S, hd, _scale(scale, hd),
-                                  int(bool(causal)), _dtype_code(out), _stream_handle(stream))
+    st = lib().xfa_bwd_preprocess(out.data_ptr(), dout.data_ptr(), delta.data_ptr(), B, H, S, hd,
+                                  _scale(scale, hd), int(bool(causal)), _dtype_code(out),
+                                  _stream_handle(stream))
     _raise(st, "xfa_bwd_preprocess")
 
 
-def _ptr(t):
-    return None if t is None else t.data_ptr()
-
-
-def _check_workspace(ref, workspace):
-    B, H, S, hd = ref.shape
-    need = xfa_bwd_workspace_bytes(B, H, S, hd, _dtype_code(ref))
-    if need:
-        if workspace is None:
-            raise ValueError(f"the backward needs a {need}-byte workspace")
-        _check_same(ref, workspace, names=("workspace",))
-        have = workspace.numel() * workspace.element_size()
-        if have < need:
-            raise ValueError(f"workspace has {have} bytes, needs {need}")
-
-
-def xfa_bwd_workspace_bytes(B, H, S, hd, dtype) -> int:
-    code = dtype if isinstance(dtype, int) else _dtype_code(_torch().empty(0, dtype=dtype))
-    return int(lib().xfa_bwd_workspace_bytes(B, H, S, hd, code))
-
-
-def xfa_bwd(q, k, v, dout, lse, delta, dq, dk, dv, workspace, scale=None, causal=True,
-            stream=None) -> None:
-    """dq, dk, dv <- gradients; ``workspace`` as cleared by xfa_bwd_preprocess."""
+def xfa_bwd(q, k, v, dout, lse, delta, dq, dk, dv, scale=None, causal=True, stream=None) -> None:
+    """dq, dk, dv <- gradients of sum(dout * out)."""
     torch = _torch()
     B, H, S, hd = q.shape
     _check_same(q, q, k, v, dout, dq, dk, dv, shape=q.shape, dtype=q.dtype,
                 names=("q", "k", "v", "dout", "dq", "dk", "dv"))
     _check_same(q, lse, delta, shape=(B, H, S), dtype=torch.float32, names=("lse", "delta"))
-    _check_workspace(q, workspace)
     st = lib().xfa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(), lse.data_ptr(),
-                       delta.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), _ptr(workspace),
+                       delta.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
                        B, H, S, hd, _scale(scale, hd), int(bool(causal)), _dtype_code(q),
                        _stream_handle(stream))
     _raise(st, "xfa_bwd")
-
-
-def workspace_for(q):
-    """A GPU byte tensor large enough for the backward of q's shape and dtype."""
-    torch = _torch()
-    B, H, S, hd = q.shape
-    need = xfa_bwd_workspace_bytes(B, H, S, hd, _dtype_code(q))
-    return torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
 
 
 # ------------------------------------------------------------ conveniences
@@ -187,13 +153,12 @@ def forward(q, k, v, scale=None, causal=True, stream=None):
     return out, lse
 
 
-def backward(q, k, v, out, dout, lse, scale=None, causal=True, stream=None, workspace=None):
+def backward(q, k, v, out, dout, lse, scale=None, causal=True, stream=None):
     """Run the preprocess and the backward; allocate and return (dq, dk, dv)."""
     torch = _torch()
     B, H, S, hd = q.shape
     delta = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
-    ws = workspace_for(q) if workspace is None else workspace
-    xfa_bwd_preprocess(out, dout, delta, ws, scale, causal, stream)
+    xfa_bwd_preprocess(out, dout, delta, scale, causal, stream)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    xfa_bwd(q, k, v, dout, lse, delta, dq, dk, dv, ws, scale, causal, stream)
+    xfa_bwd(q, k, v, dout, lse, delta, dq, dk, dv, scale, causal, stream)
     return dq, dk, dv

@@ -27,6 +27,8 @@ xfa_status_t check_common(int64_t B, int64_t H, int64_t S, int64_t hd, float sca
   // the kernels index positions with int and launch one workgroup per
   // (head, 32..128-row tile) on a 1-D grid
   if (S > (int64_t(1) << 30)) return XFA_ERR_UNSUPPORTED;
+  // one head of one fp32 tensor must fit a 32-bit byte range
+  if (S * hd * 4 > int64_t(INT32_MAX)) return XFA_ERR_UNSUPPORTED;
   if (B > 0 && H > INT64_MAX / B) return XFA_ERR_UNSUPPORTED;
   const int64_t BH = B * H;
   if (BH > 0 && (S + 31) / 32 > int64_t(INT32_MAX) / BH) return XFA_ERR_UNSUPPORTED;
@@ -61,36 +63,26 @@ xfa_status_t xfa_fwd(const void* q, const void* k, const void* v, void* out, flo
   return from_hip(xfa::launch_fwd(a));
 }
 
-xfa_status_t xfa_bwd_preprocess(const void* out, const void* dout, float* delta, void* workspace,
-                                int64_t B, int64_t H, int64_t S, int64_t hd, float scale,
-                                int causal, int dtype, void* stream) {
+xfa_status_t xfa_bwd_preprocess(const void* out, const void* dout, float* delta, int64_t B,
+                                int64_t H, int64_t S, int64_t hd, float scale, int causal,
+                                int dtype, void* stream) {
   Shape sh;
   xfa_status_t st = check_common(B, H, S, hd, scale, causal, dtype, &sh);
   if (st != XFA_OK || sh.empty) return st;
-  if ((st = check_ptrs({out, dout, delta, workspace})) != XFA_OK) return st;
-  xfa::Workspace ws;
-  xfa::bwd_workspace(workspace, sh.BH, sh.S, sh.hd, sh.bf16, &ws);
-  xfa::PreArgs a{out, dout, delta, ws, sh.BH, sh.S, sh.hd, sh.bf16, (hipStream_t)stream};
+  if ((st = check_ptrs({out, dout, delta})) != XFA_OK) return st;
+  xfa::PreArgs a{out, dout, delta, sh.BH, sh.S, sh.hd, sh.bf16, (hipStream_t)stream};
   return from_hip(xfa::launch_bwd_preprocess(a));
-}
-
-size_t xfa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t S, int64_t hd, int dtype) {
-  Shape sh;
-  if (check_common(B, H, S, hd, 1.f, 1, dtype, &sh) != XFA_OK || sh.empty) return 0;
-  return xfa::bwd_workspace(nullptr, sh.BH, sh.S, sh.hd, sh.bf16, nullptr);
 }
 
 xfa_status_t xfa_bwd(const void* q, const void* k, const void* v, const void* dout,
                      const float* lse, const float* delta, void* dq, void* dk, void* dv,
-                     void* workspace, int64_t B, int64_t H, int64_t S, int64_t hd, float scale,
-                     int causal, int dtype, void* stream) {
+                     int64_t B, int64_t H, int64_t S, int64_t hd, float scale, int causal,
+                     int dtype, void* stream) {
   Shape sh;
   xfa_status_t st = check_common(B, H, S, hd, scale, causal, dtype, &sh);
   if (st != XFA_OK || sh.empty) return st;
-  if ((st = check_ptrs({q, k, v, dout, lse, delta, dq, dk, dv, workspace})) != XFA_OK) return st;
-  xfa::Workspace ws;
-  xfa::bwd_workspace(workspace, sh.BH, sh.S, sh.hd, sh.bf16, &ws);
-  xfa::BwdArgs a{q, k, v, dout, lse, delta, dq, dk, dv, ws,
+  if ((st = check_ptrs({q, k, v, dout, lse, delta, dq, dk, dv})) != XFA_OK) return st;
+  xfa::BwdArgs a{q, k, v, dout, lse, delta, dq, dk, dv,
                  sh.BH, sh.S, sh.hd, scale, causal, sh.bf16, (hipStream_t)stream};
   return from_hip(xfa::launch_bwd(a));
 }

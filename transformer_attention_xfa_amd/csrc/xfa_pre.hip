@@ -1,4 +1,4 @@
-// Backward preprocess: D and the backward's cleared accumulator.
+// Backward preprocess: D = rowsum(dO * O).
 //
 // D_i = sum_d dO_i[d] * O_i[d]  (T14 flash-attention design doc, "What
 // flash-attention is", backward part, and Key Design Decision 3: the softmax
@@ -6,11 +6,6 @@
 // One row of O / dO is spread over the lanes that hold its 16-byte chunks;
 // each thread keeps several rows' loads in flight, sums its chunk in fp32 and
 // the row is finished with a butterfly over those lanes.
-//
-// The same pass clears the backward's workspace: the lanes that read a row's
-// chunk also zero that row's slice of the fp32 dQ accumulator, and the first
-// threads zero the per-tile arrival counters.  This keeps the backward itself
-// a single kernel and adds only a streaming write to an HBM-bound pass.
 #include "xfa_common.h"
 #include "xfa_launch.h"
 
@@ -21,17 +16,13 @@ constexpr int kPreUnroll = 4;
 
 template <typename T, int HD>
 __global__ __launch_bounds__(kPreThreads) void bwd_pre_kernel(
-    const T* __restrict__ O, const T* __restrict__ dO, float* __restrict__ Dl, float* __restrict__ dq_acc,
-    unsigned* __restrict__ counters, int64_t n_counters, int64_t nrows) {
+    const T* __restrict__ O, const T* __restrict__ dO, float* __restrict__ Dl, int64_t nrows) {
   constexpr int VE = Vec16<T>::N;
   constexpr int LPR = HD / VE;                     // lanes per row (power of two, <= 32)
   constexpr int RPI = kPreThreads / LPR;           // rows per workgroup per unroll step
   const int tid = threadIdx.x;
   const int sub = tid % LPR;
   const int64_t row0 = (int64_t)blockIdx.x * RPI * kPreUnroll + tid / LPR;
-
-  const int64_t gtid = (int64_t)blockIdx.x * kPreThreads + tid;
-  if (gtid < n_counters) counters[gtid] = 0u;
 
   typename Vec16<T>::type a[kPreUnroll], b[kPreUnroll];
 #pragma unroll
@@ -43,15 +34,6 @@ __global__ __launch_bounds__(kPreThreads) void bwd_pre_kernel(
     } else {
       a[u] = typename Vec16<T>::type{};
       b[u] = typename Vec16<T>::type{};
-    }
-  }
-#pragma unroll
-  for (int u = 0; u < kPreUnroll; ++u) {
-    const int64_t r = row0 + (int64_t)u * RPI;
-    if (r < nrows) {
-      f32x4* z = reinterpret_cast<f32x4*>(dq_acc + r * HD + sub * VE);
-#pragma unroll
-      for (int e = 0; e < VE / 4; ++e) z[e] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
   }
 #pragma unroll
@@ -71,12 +53,9 @@ static hipError_t launch_pre_t(const PreArgs& a) {
   constexpr int LPR = HD / Vec16<T>::N;
   constexpr int rows_per_wg = (kPreThreads / LPR) * kPreUnroll;
   const int64_t nrows = a.BH * a.S;
-  int64_t nwg = (nrows + rows_per_wg - 1) / rows_per_wg;
-  const int64_t nwg_cnt = (a.ws.n_counters + kPreThreads - 1) / kPreThreads;
-  if (nwg_cnt > nwg) nwg = nwg_cnt;
+  const int64_t nwg = (nrows + rows_per_wg - 1) / rows_per_wg;
   hipLaunchKernelGGL((bwd_pre_kernel<T, HD>), dim3((unsigned)nwg), dim3(kPreThreads), 0, a.stream,
-                     (const T*)a.out, (const T*)a.dout, a.delta, a.ws.dq_acc, a.ws.counters,
-                     a.ws.n_counters, nrows);
+                     (const T*)a.out, (const T*)a.dout, a.delta, nrows);
   return hipGetLastError();
 }
 
