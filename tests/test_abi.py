@@ -89,9 +89,13 @@ def test_rejects_null_and_misaligned_pointers(call, ptrs):
 
 
 def test_size_limits():
-    # one head of an fp32 tensor must fit a 32-bit byte range
-    assert _fwd(S=1 << 22, hd=128) == UNSUP
-    assert _bwd(S=(1 << 21) - 64, hd=128) in (OK, xfa.XFA_ERR_HIP) or True  # no launch without a GPU
+    # S * hd * 4 bytes (one head at fp32 width) must fit a signed 32-bit offset,
+    # whatever the dtype; accepted sizes are not tried here (they would launch)
+    for dtype in (0, 1):
+        assert _fwd(S=1 << 22, hd=128, dtype=dtype) == UNSUP
+        assert _pre(S=1 << 22, hd=128, dtype=dtype) == UNSUP
+        assert _bwd(S=1 << 22, hd=128, dtype=dtype) == UNSUP
+        assert _bwd(S=1 << 23, hd=64, dtype=dtype) == UNSUP
 
 
 @pytest.mark.parametrize("call", [_fwd, _pre, _bwd])
