@@ -10,24 +10,38 @@
 // follow-up is a key-block-owned dK/dV pass (Key Design Decisions, escape
 // hatches).  Here one launch holds two kinds of workgroups, each owning its
 // outputs outright, so nothing is summed across workgroups:
-//   * key workgroups, one per (head, tile of 32*NW keys): wave w keeps dK and
-//     dV of its 32 keys in registers and sweeps the query tiles from the
+//   * key workgroups, one per (head, 32*NW keys): wave w keeps dK and dV of
+//     its 32 keys in registers and sweeps the 32-query blocks from the
 //     diagonal on.  S = Q.K^T and dP = dO.V^T are formed with the lane owning
 //     a key, so dV^T += dO^T.P and dK^T += Q^T.dS take P and dS straight from
 //     registers;
-//   * query workgroups, one per (head, tile of 32*NW queries): wave w keeps dQ
-//     of its 32 queries in registers and sweeps the key tiles up to the
+//   * query workgroups, one per (head, 32*NW queries): wave w keeps dQ of its
+//     32 queries in registers and sweeps the 32-key blocks up to the
 //     diagonal, forming S^T and dP^T with the lane owning a query, so that
 //     dQ^T += K^T.dS^T takes dS^T straight from registers.
 // The query workgroups recompute S and dP (two extra contractions per pair);
 // in exchange there are no atomics, no cross-workgroup ordering and no
 // workspace, and dQ is bitwise reproducible.
 //
-// For bf16 the operands whose contraction index runs along tile rows (dO^T,
-// Q^T for the key workgroups, K^T for the query workgroups) are staged into
-// LDS transposed (TTile), so every operand fragment is one 16-byte read.
-// The factor `scale` of ds is applied once, to dK and dQ when they are
-// written.  Only tiles at the diagonal or the sequence end evaluate the mask.
+// Pipeline.  The streamed 32-row blocks (Q, dO, L, D for a key workgroup;
+// K, V for a query workgroup) rotate through three LDS buffers.  Iteration n
+// (one workgroup barrier) forms the two score contractions of block n+1,
+// writes block n+2 from registers into the buffer block n-1 used, finishes
+// block n (exponentials, dS and the gradient contractions) and issues the
+// global loads of block n+4: two staged blocks are in flight in registers,
+// so a load has more than an iteration to land.  The score contractions of
+// n+1 do not depend on block n's exponentials, so the matrix cores have work
+// while the vector units evaluate them.
+//
+// For bf16 the operands whose contraction index runs along block rows (dO^T,
+// Q^T for the key workgroups, K^T for the query workgroups) are also written
+// into LDS transposed (TTile), so every operand fragment is one 16-byte read.
+// A block is staged in units of 4 rows x one 16-byte column chunk: the four
+// 16-byte loads of a unit give both its row-major copy and, by byte permutes,
+// its transposed copy.  Rows past the sequence end load as zeros, and with
+// zero Q / dO (or K / V) rows such pairs add nothing, so only blocks at the
+// causal diagonal evaluate the mask.  The factor `scale` of ds is applied
+// once, to dK and dQ when they are written.
 #include <type_traits>
 
 #include "xfa_common.h"
@@ -43,11 +57,12 @@ struct BwdParams {
   int S; float scale; float c_log2; int causal;
 };
 
-// Tile geometry shared by both workgroup kinds.
+// Geometry shared by both workgroup kinds: streamed blocks of NB = 32 rows.
 template <typename T, int HD, int NW>
 struct BwdGeo {
   using M = Mma<T>;
   static constexpr bool BF = sizeof(T) == 2;
+  static constexpr int NB = 32;
   static constexpr int NT = NW * 64;
   static constexpr int HDP = HD < 32 ? 32 : HD;
   static constexpr int NDB = HDP / 32;           // 32-row d blocks
@@ -55,14 +70,18 @@ struct BwdGeo {
   static constexpr int NU = 32 / M::KD;          // instructions per 32-wide k block
   static constexpr int VE = Vec16<T>::N;
   static constexpr int CPR = HD / VE;            // 16-byte chunks per row
+  static constexpr int UPT = (NB / 4) * CPR;     // 4-row x 1-chunk units per block of a tensor
+  static constexpr int PFU = (2 * UPT + NT - 1) / NT;   // units per thread (two tensors)
   // row-major tiles: a row stride of 4 (mod 8) dwords reads conflict-free
   static constexpr int LD = HDP + (BF ? 8 : 4);
+  static constexpr int NE = NB * LD;             // elements of a row-major block
+  static constexpr int TE = BF ? HDP * NB : 0;   // elements of a transposed block
   static constexpr uint32_t ROWB = HD * sizeof(T);
   static_assert(HD % M::KD == 0 && HD % VE == 0, "unsupported head dim");
 };
+using TB = TTile<32>;
 
-// Four rows x two bf16 columns of a row-major tile -> a transposed tile.
-template <typename TT>
+// Four rows x two bf16 columns of a block -> the transposed block.
 __device__ inline void put_t(unsigned* t, int c, int r, const unsigned x[4]) {
   u32x2 col0, col1;
   transpose_4x2(x, col0, col1);
@@ -70,9 +89,145 @@ __device__ inline void put_t(unsigned* t, int c, int r, const unsigned x[4]) {
   const bool odd_first = (lane() >> 3) & 1;
   const int c_first = c + (odd_first ? 1 : 0);
   const int dw_half = 2 * ((p >> 2) & 1);
-  *reinterpret_cast<u32x2*>(t + TT::chunk_dw(c_first, p >> 3) + dw_half) = odd_first ? col1 : col0;
-  *reinterpret_cast<u32x2*>(t + TT::chunk_dw(c_first ^ 1, p >> 3) + dw_half) = odd_first ? col0 : col1;
+  *reinterpret_cast<u32x2*>(t + TB::chunk_dw(c_first, p >> 3) + dw_half) = odd_first ? col1 : col0;
+  *reinterpret_cast<u32x2*>(t + TB::chunk_dw(c_first ^ 1, p >> 3) + dw_half) = odd_first ? col0 : col1;
 }
+
+// Global loads of the streamed blocks are issued through inline assembly and
+// waited for explicitly: the compiler's own wait-count placement merges the
+// states of the unrolled loop bodies conservatively and then waits for every
+// load in flight, including the ones issued just before, which exposes the
+// full load latency once per iteration.  These loads are the only vector
+// memory operations inside the loops; every load the compiler issues itself
+// (the per-lane K/V or Q/dO rows) has been waited for before the first of
+// them (see settle()).  The compiler takes an asm load's result register as
+// written when the instruction issues, so every such register is kept live
+// (used by a settle() after the matching wait) until its load has landed;
+// otherwise it could hand the register to another value that the late load
+// data would then overwrite.
+typedef unsigned u32x4s __attribute__((ext_vector_type(4)));
+
+// A raw buffer descriptor in scalar registers: 48-bit base, no stride,
+// nbytes records, 32-bit raw data (same fields make_buffer_rsrc produces).
+__device__ inline u32x4s make_desc(const void* base, uint32_t nbytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return u32x4s{(unsigned)__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
+                (unsigned)__builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu)),
+                (unsigned)__builtin_amdgcn_readfirstlane((int)nbytes), (unsigned)kRsrcWord3};
+}
+// The loads are volatile (never removed, duplicated or moved across another
+// volatile statement or memory access), so the count of loads issued after a
+// set is exactly what the code says; a load's result is only read through the
+// wait that covers it (wait_vm with the registers as operands).
+__device__ inline u32x4 asm_load16(const u32x4s& d, uint32_t off) {
+  u32x4 r;
+  asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen" : "=v"(r) : "v"(off), "s"(d));
+  return r;
+}
+__device__ inline float asm_load4(const u32x4s& d, uint32_t off) {
+  float r;
+  asm volatile("buffer_load_dword %0, %1, %2, 0 offen" : "=v"(r) : "v"(off), "s"(d));
+  return r;
+}
+// Wait until at most N of this wave's vector memory operations are in flight.
+template <int N>
+__device__ inline void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N));
+}
+// The same wait, also marking the registers of the loads it covers as
+// (re)defined by it, so that no use of them can move above it.
+template <int N>
+__device__ inline void wait_vm(u32x4 (&x)[1][4]) {
+  asm volatile("s_waitcnt vmcnt(%4)" : "+v"(x[0][0]), "+v"(x[0][1]), "+v"(x[0][2]), "+v"(x[0][3]) : "n"(N));
+}
+template <int N>
+__device__ inline void wait_vm(u32x4 (&x)[2][4]) {
+  asm volatile("s_waitcnt vmcnt(%8)"
+               : "+v"(x[0][0]), "+v"(x[0][1]), "+v"(x[0][2]), "+v"(x[0][3]), "+v"(x[1][0]), "+v"(x[1][1]),
+                 "+v"(x[1][2]), "+v"(x[1][3])
+               : "n"(N));
+}
+template <int N>
+__device__ inline void wait_vm(u32x4 (&x)[1][4], float& a, float& b) {
+  asm volatile("s_waitcnt vmcnt(%6)"
+               : "+v"(x[0][0]), "+v"(x[0][1]), "+v"(x[0][2]), "+v"(x[0][3]), "+v"(a), "+v"(b)
+               : "n"(N));
+}
+template <int N>
+__device__ inline void wait_vm(u32x4 (&x)[2][4], float& a, float& b) {
+  asm volatile("s_waitcnt vmcnt(%10)"
+               : "+v"(x[0][0]), "+v"(x[0][1]), "+v"(x[0][2]), "+v"(x[0][3]), "+v"(x[1][0]), "+v"(x[1][1]),
+                 "+v"(x[1][2]), "+v"(x[1][3]), "+v"(a), "+v"(b)
+               : "n"(N));
+}
+// Mark a register as (re)defined here, after the preceding wait: uses of it
+// cannot move above this point.
+template <typename X>
+__device__ inline void settle(X& x) {
+  asm volatile("" : "+v"(x));
+}
+
+// Staging of one block of two tensors A and B ([S][HD] rows row0..row0+31) in
+// 4-row x 1-chunk units, rows fastest across lanes: unit u of a tensor covers
+// rows 4*(u % 8) .. +3 and chunk u / 8.  The first NW/2 waves stage A and
+// the others B, so the tensor is wave-uniform.  Every thread issues exactly
+// NLOAD loads per block (threads without a unit read past the buffer end,
+// which returns zeros), so all waves count the same loads in flight.  A (B)
+// is also written transposed when TRA (TRB) is set (bf16 only).
+template <typename T, int HD, int NW, bool TRA, bool TRB>
+struct Stage2 {
+  using G = BwdGeo<T, HD, NW>;
+  static constexpr int HALF = G::NT / 2;                   // threads per tensor
+  static constexpr int PFU = (G::UPT + HALF - 1) / HALF;   // units per thread
+  static constexpr int NLOAD = 4 * PFU;
+  u32x4 x[PFU][4];
+
+  __device__ static inline bool wave_a() { return __builtin_amdgcn_readfirstlane((int)threadIdx.x) < HALF; }
+  __device__ static inline int unit(int i) { return (int)(threadIdx.x % HALF) + i * HALF; }
+
+  __device__ inline void load(const u32x4s& da, const u32x4s& db, int row0) {
+    const u32x4s d = wave_a() ? da : db;
+#pragma unroll
+    for (int i = 0; i < PFU; ++i) {
+      const int u = unit(i);
+      const uint32_t off = (G::UPT % HALF == 0 || u < G::UPT)
+                               ? (uint32_t)(row0 + 4 * (u & 7)) * G::ROWB + (uint32_t)(u >> 3) * 16u
+                               : 0x80000000u;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) x[i][k] = asm_load16(d, off + k * G::ROWB);
+    }
+  }
+  __device__ inline void settle_all() {
+#pragma unroll
+    for (int i = 0; i < PFU; ++i)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) settle(x[i][k]);
+  }
+  // a, b: row-major blocks (row stride LD); at, bt: their transposed blocks
+  __device__ inline void store(T* a, T* b, T* at, T* bt) const {
+    const bool is_a = wave_a();
+#pragma unroll
+    for (int i = 0; i < PFU; ++i) {
+      const int u = unit(i);
+      if (G::UPT % HALF == 0 || u < G::UPT) {
+        const int r = 4 * (u & 7), c = (u >> 3) * G::VE;
+        T* dst = (is_a ? a : b) + r * G::LD + c;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) *reinterpret_cast<u32x4*>(dst + k * G::LD) = x[i][k];
+        if constexpr ((TRA || TRB) && G::BF) {
+          if ((TRA && is_a) || (TRB && !is_a)) {
+            unsigned* t = reinterpret_cast<unsigned*>(is_a ? at : bt);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+              const unsigned col[4] = {x[i][0][m], x[i][1][m], x[i][2][m], x[i][3][m]};
+              put_t(t, c + 2 * m, r, col);
+            }
+          }
+        }
+      }
+    }
+  }
+};
 
 // Four consecutive C-tile results, scaled, to one row of an output tensor.
 template <typename T>
@@ -80,39 +235,95 @@ __device__ inline void store4(rsrc_t r, uint32_t off, const f32x16& a, int g, fl
   bstore_row4(r, off, a[4 * g] * s, a[4 * g + 1] * s, a[4 * g + 2] * s, a[4 * g + 3] * s, T{});
 }
 
-// ------------------------------------------------------------ key workgroups
-template <typename T, int HD, int NW, int BQ>
-struct KeyTiles {
+// Zero the d >= HD padding of the blocks (hd = 16 only); padded rows and
+// columns feed only C-tile rows that are never stored.
+template <typename T, int HD, int NW>
+__device__ inline void zero_pad(T* nat, T* tr) {
   using G = BwdGeo<T, HD, NW>;
-  static constexpr int QE = BQ * G::LD;                    // elements of a row-major Q / dO tile
-  static constexpr int TE = G::BF ? G::HDP * BQ : 0;       // elements of a transposed tile
-  static constexpr size_t BYTES = (2 * QE + 2 * TE) * sizeof(T) + 2 * BQ * sizeof(float);
+  if constexpr (G::HDP != HD) {
+    for (int e = threadIdx.x; e < G::NB * (G::HDP - HD); e += G::NT) {
+      const int r = e / (G::HDP - HD), c = HD + e % (G::HDP - HD);
+      nat[r * G::LD + c] = (T)0.f;
+    }
+    if constexpr (G::BF)
+      for (int e = threadIdx.x; e < (G::HDP - HD) * G::NB; e += G::NT) tr[HD * G::NB + e] = (T)0.f;
+  }
+}
+
+// Two sets of score tiles alternate between "block n being finished" and
+// "block n+1 being formed"; which set plays which part is the iteration's
+// parity, a compile-time constant in every loop body (loops are unrolled by
+// two by hand: the workgroup barrier in the body keeps the compiler from
+// unrolling them itself), so no tile is ever copied.
+struct Pipe {
+  struct Pair { f32x16& s; f32x16& dp; };
+  Pair p0, p1;
+  __device__ Pipe(f32x16& s0, f32x16& d0, f32x16& s1, f32x16& d1) : p0{s0, d0}, p1{s1, d1} {}
+  template <int P> __device__ Pair cur(std::integral_constant<int, P>) { return P ? p1 : p0; }
+  template <int P> __device__ Pair next(std::integral_constant<int, P>) { return P ? p0 : p1; }
+  // Iterations [n, end) of body(masked, parity, n), starting at parity 0;
+  // par becomes the parity after them.  Callers start a run only at parity 0
+  // (every run but the last has an even length), so at the entry of a body of
+  // parity P the staged set P was always issued before set 1-P, which is
+  // what the body's wait count relies on.
+  template <typename Body, typename Masked>
+  __device__ void run(Body& body, Masked m, int& n, int end, int& par) {
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    if (n >= end) return;
+    for (; n + 1 < end; n += 2) {
+      body(m, P0{}, n);
+      body(m, P1{}, n + 1);
+    }
+    par = 0;
+    if (n < end) {
+      body(m, P0{}, n);
+      ++n;
+      par = 1;
+    }
+  }
+  // the final block: finish(masked, n, s, dp) without a successor
+  template <typename Finish>
+  __device__ void last(Finish& finish, bool masked, int n, int par) {
+    if (par) {
+      if (masked) finish(std::true_type{}, n, p1.s, p1.dp);
+      else finish(std::false_type{}, n, p1.s, p1.dp);
+    } else {
+      if (masked) finish(std::true_type{}, n, p0.s, p0.dp);
+      else finish(std::false_type{}, n, p0.s, p0.dp);
+    }
+  }
 };
 
-template <typename T, int HD, int NW, int BQ>
+// ------------------------------------------------------------ key workgroups
+// One LDS buffer: row-major Q and dO blocks, their transposes (bf16), and the
+// block's L * log2(e) and D.
+template <typename T, int HD, int NW>
+struct KeyBuf {
+  using G = BwdGeo<T, HD, NW>;
+  static constexpr size_t BYTES = (2 * G::NE + 2 * G::TE) * sizeof(T) + 2 * G::NB * sizeof(float);
+  T* q; T* dO; T* qt; T* dOt; float* L; float* D;
+  __device__ KeyBuf(char* base) {
+    q = reinterpret_cast<T*>(base);
+    dO = q + G::NE;
+    qt = dO + G::NE;
+    dOt = qt + G::TE;
+    L = reinterpret_cast<float*>(dOt + G::TE);
+    D = L + G::NB;
+  }
+};
+
+template <typename T, int HD, int NW>
 __device__ __forceinline__ void key_role(const BwdParams<T>& p, int bh, int kt, char* smem) {
   using G = BwdGeo<T, HD, NW>;
   using M = typename G::M;
-  using KT_ = KeyTiles<T, HD, NW, BQ>;
-  using TQ = TTile<BQ>;
+  using KB = KeyBuf<T, HD, NW>;
   constexpr bool BF = G::BF;
-  constexpr int NT = G::NT, HDP = G::HDP, NDB = G::NDB, NC = G::NC, NU = G::NU;
-  constexpr int VE = G::VE, CPR = G::CPR, LD = G::LD;
+  constexpr int NB = G::NB, NDB = G::NDB, NC = G::NC, NU = G::NU, LD = G::LD;
   constexpr uint32_t ROWB = G::ROWB;
   constexpr int BKV = NW * 32;
-  constexpr int NQB = BQ / 32;
-  constexpr int QCH = BQ * CPR;                  // 16-byte chunks of a Q tile
-  constexpr int PF = (QCH + NT - 1) / NT;
-  constexpr int QUN = (BQ / 4) * (HD / 2);       // 4-row x 2-column units of a Q tile
-  constexpr int PFT = BF ? (QUN + NT - 1) / NT : 1;
-  static_assert(BQ <= NT, "L/D staging assumes one thread per query");
-
-  T* Qs = reinterpret_cast<T*>(smem);
-  T* dOs = Qs + KT_::QE;
-  T* QT = dOs + KT_::QE;
-  T* dOT = QT + KT_::TE;
-  float* Ls = reinterpret_cast<float*>(dOT + KT_::TE);
-  float* Ds = Ls + BQ;
+  static_assert(NB <= G::NT, "L/D staging assumes one thread per query");
+  static_assert((BKV / NB) % 2 == 0, "the diagonal run must have an even length");
 
   const int S = p.S;
   const int tid = threadIdx.x, l = lane(), h = l >> 5, w = tid >> 6;
@@ -126,23 +337,19 @@ __device__ __forceinline__ void key_role(const BwdParams<T>& p, int bh, int kt, 
   const rsrc_t rD = make_rsrc(p.Dl + (size_t)bh * S, (uint32_t)S * 4u);
 
   const int j0 = kt * BKV;                       // first key of the workgroup
-  const int jw0 = j0 + 32 * w;                   // first key of this wave
-  const int kj = jw0 + (l & 31);                 // this lane's key
-  const bool wave_live = jw0 < S;
-  const int nqt = (S + BQ - 1) / BQ;
-  const int qt_first = p.causal ? j0 / BQ : 0;
-  // queries that see this lane's key: [q_lo, q_hi)
-  const int q_lo = p.causal ? kj : 0;
-  const int q_hi = kj < S ? S : 0;
+  const int kj = j0 + 32 * w + (l & 31);         // this lane's key
+  const int nb = (S + NB - 1) / NB;              // query blocks
+  const int n0 = p.causal ? j0 / NB : 0;         // first block that sees a key here
+  // blocks [n0, nm) cross the diagonal of this workgroup's keys
+  const int nm = p.causal ? min(nb, n0 + BKV / NB) : n0;
+  const int nl = nb - 1;
 
-  if constexpr (HDP != HD) {   // padding (d >= HD) stays zero
-    for (int e = tid; e < BQ * (HDP - HD); e += NT) {
-      const int r = e / (HDP - HD), c = HD + e % (HDP - HD);
-      Qs[r * LD + c] = (T)0.f;
-      dOs[r * LD + c] = (T)0.f;
-    }
-    if constexpr (BF)
-      for (int e = tid; e < (HDP - HD) * BQ; e += NT) QT[HD * BQ + e] = dOT[HD * BQ + e] = (T)0.f;
+  auto buf = [&](int n) { return KB(smem + (size_t)(n % 3) * KB::BYTES); };
+#pragma unroll
+  for (int b = 0; b < 3; ++b) {
+    KB kb(smem + b * KB::BYTES);
+    zero_pad<T, HD, NW>(kb.q, kb.qt);
+    zero_pad<T, HD, NW>(kb.dO, kb.dOt);
   }
 
   // this lane's key row of K and V: B operands of S = Q.K^T and dP = dO.V^T
@@ -166,150 +373,133 @@ __device__ __forceinline__ void key_role(const BwdParams<T>& p, int bh, int kt, 
     dvacc[d] = zero16();
   }
 
-  // the next query tile in flight: row-major chunks and (bf16) 4x2 units
-  typename Vec16<T>::type pq[PF], pd[PF];
-  unsigned tq[PFT][4], td[PFT][4];
-  float pl = 0.f, pdl = 0.f;
-  auto prefetch = [&](int qt) {
-    const int q0 = qt * BQ;
-#pragma unroll
-    for (int i = 0; i < PF; ++i) {
-      const int e = tid + i * NT;
-      const int r = e / CPR, c = (e - r * CPR) * VE;
-      const uint32_t off = (uint32_t)(q0 + r) * ROWB + c * sizeof(T);
-      if (QCH % NT == 0 || e < QCH) {
-        pq[i] = bload16<T>(rQ, off);   // rows past the end read as zeros
-        pd[i] = bload16<T>(rdO, off);
-      }
-    }
-    if constexpr (BF) {
-#pragma unroll
-      for (int i = 0; i < PFT; ++i) {
-        const int e = tid + i * NT;
-        const int cp = e % (HD / 2), rg = e / (HD / 2);
-        const uint32_t off = (uint32_t)(q0 + 4 * rg) * ROWB + cp * 4u;
-        if (QUN % NT == 0 || e < QUN) {
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            tq[i][k] = __float_as_uint(bload4(rQ, off + k * ROWB));
-            td[i][k] = __float_as_uint(bload4(rdO, off + k * ROWB));
-          }
-        }
-      }
-    }
-    if (tid < BQ) {
-      pl = bload4(rL, (uint32_t)(q0 + tid) * 4u) * kLog2e;
-      pdl = bload4(rD, (uint32_t)(q0 + tid) * 4u);
-    }
+  // staged blocks in flight (set P holds the block written in iterations of
+  // parity P); L and D are loaded by every thread (row tid % 32) so that all
+  // waves count the same loads
+  using St = Stage2<T, HD, NW, true, true>;
+  struct Staged {
+    St x;
+    float l = 0.f, d = 0.f;
+  } a[2];
+  constexpr int NLOAD = St::NLOAD + 2;           // loads per staged block
+  const u32x4s dQd = make_desc(p.Q + hoff, head_bytes), ddOd = make_desc(p.dO + hoff, head_bytes);
+  const u32x4s dLd = make_desc(p.Lse + (size_t)bh * S, (uint32_t)S * 4u);
+  const u32x4s dDd = make_desc(p.Dl + (size_t)bh * S, (uint32_t)S * 4u);
+  auto load = [&](Staged& z, int n) {
+    z.x.load(dQd, ddOd, n * NB);
+    z.l = asm_load4(dLd, (uint32_t)(n * NB + (tid & (NB - 1))) * 4u);
+    z.d = asm_load4(dDd, (uint32_t)(n * NB + (tid & (NB - 1))) * 4u);
   };
-  auto stage = [&]() {
+  // wait until at most N loads are in flight, which lands set z
+  auto ready = [&](auto n_after, Staged& z) { wait_vm<decltype(n_after)::value>(z.x.x, z.l, z.d); };
+  using Zero = std::integral_constant<int, 0>;
+  using One = std::integral_constant<int, NLOAD>;
+  // S and dP of block n: C tiles with column = this lane's key, rows = queries
+  auto sdp = [&](int n, f32x16& s, f32x16& dp) {
+    KB b = buf(n);
+    const T* qrow = b.q + (l & 31) * LD + M::KW * h;
+    const T* dorow = b.dO + (l & 31) * LD + M::KW * h;
+    s = zero16();
+    dp = zero16();
 #pragma unroll
-    for (int i = 0; i < PF; ++i) {
-      const int e = tid + i * NT;
-      if (QCH % NT == 0 || e < QCH) {
-        const int r = e / CPR, c = (e - r * CPR) * VE;
-        st16(Qs + r * LD + c, pq[i]);
-        st16(dOs + r * LD + c, pd[i]);
-      }
-    }
-    if constexpr (BF) {
-#pragma unroll
-      for (int i = 0; i < PFT; ++i) {
-        const int e = tid + i * NT;
-        if (QUN % NT == 0 || e < QUN) {
-          const int cp = e % (HD / 2), rg = e / (HD / 2);
-          put_t<TQ>(reinterpret_cast<unsigned*>(QT), 2 * cp, 4 * rg, tq[i]);
-          put_t<TQ>(reinterpret_cast<unsigned*>(dOT), 2 * cp, 4 * rg, td[i]);
-        }
-      }
-    }
-    if (tid < BQ) {
-      Ls[tid] = pl;
-      Ds[tid] = pdl;
+    for (int c = 0; c < NC; ++c) {
+      s = M::mma(ld_nat(qrow + c * M::KD), kf[c], s);
+      dp = M::mma(ld_nat(dorow + c * M::KD), vf[c], dp);
     }
   };
 
-  // one query tile: dV and dK updates of this wave's keys
-  auto compute = [&](auto masked, int qt) {
-    const int q0 = qt * BQ;
-    const int q_last = min(q0 + BQ, S) - 1;
-    // keys of this wave all above the diagonal of this query tile: nothing to add
-    if (!wave_live || (p.causal && jw0 > q_last)) return;
+  // p = 2^(s c - L log2 e), dS = p (dp - D); dV^T += dO^T.P, dK^T += Q^T.dS
+  auto finish = [&](auto masked, int n, f32x16 s, f32x16 dp) {
+    KB b = buf(n);
 #pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) {
-      f32x16 sacc = zero16(), pacc = zero16();
-      const T* qrow = Qs + (qb * 32 + (l & 31)) * LD + M::KW * h;
-      const T* dorow = dOs + (qb * 32 + (l & 31)) * LD + M::KW * h;
+    for (int g = 0; g < 4; ++g) {
+      const f32x4 L4 = *reinterpret_cast<const f32x4*>(b.L + 8 * g + 4 * h);
+      const f32x4 D4 = *reinterpret_cast<const f32x4*>(b.D + 8 * g + 4 * h);
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        sacc = M::mma(ld_nat(qrow + c * M::KD), kf[c], sacc);
-        pacc = M::mma(ld_nat(dorow + c * M::KD), vf[c], pacc);
+      for (int e = 0; e < 4; ++e) {
+        const int v = 4 * g + e;
+        const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[v], p.c_log2, -L4[e]));
+        s[v] = pr;
+        dp[v] = pr * (dp[v] - D4[e]);
       }
-      // p = 2^(s c - L log2 e), dS = p (dp - D)
+    }
+    if constexpr (decltype(masked)::value) {
+      // query q sees key kj iff q >= kj
+      const int lo = kj - (n * NB + 4 * h);
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int r0 = qb * 32 + 8 * g + 4 * h;
-        const f32x4 L4 = *reinterpret_cast<const f32x4*>(Ls + r0);
-        const f32x4 D4 = *reinterpret_cast<const f32x4*>(Ds + r0);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int v = 4 * g + e;
-          const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[v], p.c_log2, -L4[e]));
-          sacc[v] = pr;
-          pacc[v] = pr * (pacc[v] - D4[e]);
-        }
+      for (int v = 0; v < 16; ++v) {
+        const bool keep = 8 * (v >> 2) + (v & 3) >= lo;
+        s[v] = keep ? s[v] : 0.f;
+        dp[v] = keep ? dp[v] : 0.f;
       }
-      if constexpr (decltype(masked)::value) {
-        // masked pairs give p = 0 and dS = 0
-        const int base = q0 + qb * 32 + 4 * h;
-        const int lo = q_lo - base, hi = q_hi - base;
+    }
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int rel = 8 * (v >> 2) + (v & 3);
-          const bool keep = (rel >= lo) & (rel < hi);
-          sacc[v] = keep ? sacc[v] : 0.f;
-          pacc[v] = keep ? pacc[v] : 0.f;
+    for (int u = 0; u < NU; ++u) {
+      const typename M::frag pf = frag_from_acc(s, u, T{});
+      const typename M::frag sf = frag_from_acc(dp, u, T{});
+#pragma unroll
+      for (int d = 0; d < NDB; ++d) {
+        typename M::frag af, bf;
+        if constexpr (BF) {
+          const int c = d * 32 + (l & 31);
+          af = *reinterpret_cast<const bf16x8*>(b.dOt + 2 * TB::chunk_dw(c, 2 * u + h));
+          bf = *reinterpret_cast<const bf16x8*>(b.qt + 2 * TB::chunk_dw(c, 2 * u + h));
+        } else {
+          af = ld_res(b.dO, LD, 0, u, d * 32);
+          bf = ld_res(b.q, LD, 0, u, d * 32);
         }
-      }
-      // dV^T += dO^T . P,  dK^T += Q^T . dS   (k runs over the block's queries)
-#pragma unroll
-      for (int u = 0; u < NU; ++u) {
-        const typename M::frag pf = frag_from_acc(sacc, u, T{});
-        const typename M::frag sf = frag_from_acc(pacc, u, T{});
-#pragma unroll
-        for (int d = 0; d < NDB; ++d) {
-          typename M::frag af, bf;
-          if constexpr (BF) {
-            const int c = d * 32 + (l & 31);
-            const int j = 4 * qb + 2 * u + h;
-            af = *reinterpret_cast<const bf16x8*>(dOT + 2 * TQ::chunk_dw(c, j));
-            bf = *reinterpret_cast<const bf16x8*>(QT + 2 * TQ::chunk_dw(c, j));
-          } else {
-            af = ld_res(dOs, LD, qb * 32, u, d * 32);
-            bf = ld_res(Qs, LD, qb * 32, u, d * 32);
-          }
-          dvacc[d] = M::mma(af, pf, dvacc[d]);
-          dkacc[d] = M::mma(bf, sf, dkacc[d]);
-        }
+        dvacc[d] = M::mma(af, pf, dvacc[d]);
+        dkacc[d] = M::mma(bf, sf, dkacc[d]);
       }
     }
   };
 
-  auto step = [&](auto masked, int qt) {
-    __syncthreads();          // all waves done with the previous tile
-    stage();
+  auto put = [&](const Staged& z, int n) {
+    KB b = buf(n);
+    z.x.store(b.q, b.dO, b.qt, b.dOt);
+    if (tid < NB) {
+      b.L[tid] = z.l * kLog2e;   // L in log2 units (the load has landed: see ready())
+      b.D[tid] = z.d;
+    }
+  };
+
+  // the compiler's own loads (kf, vf) land before the staging loads start
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    settle(kf[c]);
+    settle(vf[c]);
+  }
+  f32x16 sa, pa, sb, pb;
+  load(a[0], n0);
+  ready(Zero{}, a[0]);
+  put(a[0], n0);
+  load(a[0], n0 + 1);
+  ready(Zero{}, a[0]);
+  put(a[0], n0 + 1);
+  load(a[0], n0 + 2);
+  load(a[1], n0 + 3);
+  __syncthreads();
+  sdp(n0, sa, pa);
+  Pipe pipe(sa, pa, sb, pb);
+  auto body = [&](auto masked, auto par, int n) {
+    constexpr int P = decltype(par)::value;
+    ready(One{}, a[P]);        // set P landed; set 1-P (one block behind) in flight
+    sdp(n + 1, pipe.next(par).s, pipe.next(par).dp);
+    put(a[P], n + 2);
+    finish(masked, n, pipe.cur(par).s, pipe.cur(par).dp);
+    load(a[P], n + 4);         // last: volatile loads order the memory accesses around them
     __syncthreads();
-    if (qt + 1 < nqt) prefetch(qt + 1);
-    compute(masked, qt);
   };
-
-  // query tiles in [qt_mid0, qt_mid1) are unmasked for every key of the workgroup
-  const int qt_mid0 = min(nqt, p.causal ? max(qt_first, (j0 + BKV - 1 + BQ - 1) / BQ) : qt_first);
-  const int qt_mid1 = max(qt_mid0, (j0 + BKV <= S) ? S / BQ : qt_mid0);   // S / BQ <= nqt
-  prefetch(qt_first);
-  for (int qt = qt_first; qt < qt_mid0; ++qt) step(std::true_type{}, qt);
-  for (int qt = qt_mid0; qt < qt_mid1; ++qt) step(std::false_type{}, qt);
-  for (int qt = qt_mid1; qt < nqt; ++qt) step(std::true_type{}, qt);
+  // causal: the first BKV/NB blocks cross the diagonal (an even count), or
+  // all of them if fewer remain; non-causal: none
+  int n = n0, par = 0;
+  pipe.run(body, std::true_type{}, n, min(nm, nl), par);
+  pipe.run(body, std::false_type{}, n, nl, par);
+  pipe.last(finish, nl < nm, nl, par);
+  // drain the loads of blocks past the end; their registers stay reserved
+  // until the loads have landed
+  ready(Zero{}, a[0]);
+  ready(Zero{}, a[1]);
 
   // dK_j (scaled), dV_j for this lane's key: C tile column = key, rows = d
   const rsrc_t rdK = make_rsrc(p.dK + hoff, head_bytes);
@@ -320,7 +510,7 @@ __device__ __forceinline__ void key_role(const BwdParams<T>& p, int bh, int kt, 
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int dd = d * 32 + 8 * g + 4 * h;
-      if (HDP == HD || dd < HD) {
+      if (G::HDP == HD || dd < HD) {
         store4<T>(rdK, krow + dd * sizeof(T), dkacc[d], g, p.scale);
         store4<T>(rdV, krow + dd * sizeof(T), dvacc[d], g, 1.f);
       }
@@ -329,37 +519,32 @@ __device__ __forceinline__ void key_role(const BwdParams<T>& p, int bh, int kt, 
 }
 
 // ---------------------------------------------------------- query workgroups
-template <typename T, int HD, int NW, int BK>
-struct QueryTiles {
+// One LDS buffer: row-major K and V blocks and the transpose of K (bf16).
+template <typename T, int HD, int NW>
+struct QueryBuf {
   using G = BwdGeo<T, HD, NW>;
-  static constexpr int KE = BK * G::LD;                    // elements of a row-major K / V tile
-  static constexpr int TE = G::BF ? G::HDP * BK : 0;       // elements of the transposed K tile
-  static constexpr size_t BYTES = (2 * KE + TE) * sizeof(T);
+  static constexpr size_t BYTES = (2 * G::NE + G::TE) * sizeof(T);
+  T* k; T* v; T* kt;
+  __device__ QueryBuf(char* base) {
+    k = reinterpret_cast<T*>(base);
+    v = k + G::NE;
+    kt = v + G::NE;
+  }
 };
 
-template <typename T, int HD, int NW, int BK>
+template <typename T, int HD, int NW>
 __device__ __forceinline__ void query_role(const BwdParams<T>& p, int bh, int qq, char* smem) {
   using G = BwdGeo<T, HD, NW>;
   using M = typename G::M;
-  using QT_ = QueryTiles<T, HD, NW, BK>;
-  using TK = TTile<BK>;
+  using QB = QueryBuf<T, HD, NW>;
   constexpr bool BF = G::BF;
-  constexpr int NT = G::NT, HDP = G::HDP, NDB = G::NDB, NC = G::NC, NU = G::NU;
-  constexpr int VE = G::VE, CPR = G::CPR, LD = G::LD;
+  constexpr int NB = G::NB, NDB = G::NDB, NC = G::NC, NU = G::NU, LD = G::LD;
   constexpr uint32_t ROWB = G::ROWB;
   constexpr int BQ = NW * 32;
-  constexpr int NKB = BK / 32;
-  constexpr int KCH = BK * CPR;
-  constexpr int PF = (KCH + NT - 1) / NT;
-  constexpr int KUN = (BK / 4) * (HD / 2);
-  constexpr int PFT = BF ? (KUN + NT - 1) / NT : 1;
-
-  T* Ks = reinterpret_cast<T*>(smem);
-  T* Vs = Ks + QT_::KE;
-  T* KTs = Vs + QT_::KE;
+  static_assert((BQ / NB) % 2 == 0, "the unmasked run must have an even length");
 
   const int S = p.S;
-  const int tid = threadIdx.x, l = lane(), h = l >> 5, w = tid >> 6;
+  const int l = lane(), h = l >> 5, w = threadIdx.x >> 6;
   const size_t hoff = (size_t)bh * S * HD;
   const uint32_t head_bytes = (uint32_t)S * ROWB;
   const rsrc_t rQ = make_rsrc(p.Q + hoff, head_bytes);
@@ -370,23 +555,19 @@ __device__ __forceinline__ void query_role(const BwdParams<T>& p, int bh, int qq
   const rsrc_t rD = make_rsrc(p.Dl + (size_t)bh * S, (uint32_t)S * 4u);
 
   const int q0 = qq * BQ;
-  const int qw0 = q0 + 32 * w;                   // first query of this wave
-  const int qi = qw0 + (l & 31);                 // this lane's query
+  const int qi = q0 + 32 * w + (l & 31);         // this lane's query
   const int q_last = min(q0 + BQ, S) - 1;
-  const int qw_last = min(qw0 + 31, S - 1);
-  const bool wave_live = qw0 < S;
-  const int n_tiles = p.causal ? (q_last / BK + 1) : ((S + BK - 1) / BK);
-  const int key_lim = p.causal ? min(qi, S - 1) : S - 1;   // last key this query sees
+  const int nb = p.causal ? q_last / NB + 1 : (S + NB - 1) / NB;   // key blocks
+  // blocks [nm, nb) cross the diagonal of this workgroup's queries
+  const int nm = p.causal ? q0 / NB : nb;
+  const int nl = nb - 1;
 
-  if constexpr (HDP != HD) {
-    if constexpr (BF) {
-      for (int e = tid; e < (HDP - HD) * BK; e += NT) KTs[HD * BK + e] = (T)0.f;
-    } else {
-      for (int e = tid; e < BK * (HDP - HD); e += NT) {
-        const int r = e / (HDP - HD), c = HD + e % (HDP - HD);
-        Ks[r * LD + c] = (T)0.f;
-      }
-    }
+  auto buf = [&](int n) { return QB(smem + (size_t)(n % 3) * QB::BYTES); };
+#pragma unroll
+  for (int b = 0; b < 3; ++b) {
+    QB qb(smem + b * QB::BYTES);
+    zero_pad<T, HD, NW>(qb.k, qb.kt);
+    zero_pad<T, HD, NW>(qb.v, qb.kt);
   }
 
   // this lane's query row of Q and dO: B operands of S^T = K.Q^T and dP^T = V.dO^T
@@ -402,124 +583,106 @@ __device__ __forceinline__ void query_role(const BwdParams<T>& p, int bh, int qq
       of[c] = bload4(rdO, off);
     }
   }
-  const float L2 = bload4(rL, (uint32_t)qi * 4u) * kLog2e;
-  const float Di = bload4(rD, (uint32_t)qi * 4u);
+  float L2 = bload4(rL, (uint32_t)qi * 4u) * kLog2e;
+  float Di = bload4(rD, (uint32_t)qi * 4u);
 
   f32x16 dqacc[NDB];
 #pragma unroll
   for (int d = 0; d < NDB; ++d) dqacc[d] = zero16();
 
-  typename Vec16<T>::type pk[PF], pv[PF];
-  unsigned tk[PFT][4];
-  auto prefetch = [&](int kt) {
+  // staged blocks in flight (set P holds the block written in iterations of parity P)
+  using St = Stage2<T, HD, NW, true, false>;
+  St a[2];
+  constexpr int NLOAD = St::NLOAD;
+  const u32x4s dKd = make_desc(p.K + hoff, head_bytes), dVd = make_desc(p.V + hoff, head_bytes);
+  auto load = [&](St& z, int n) { z.load(dKd, dVd, n * NB); };
+  auto put = [&](const St& z, int n) {
+    QB b = buf(n);
+    z.store(b.k, b.v, b.kt, nullptr);
+  };
+
+  // S^T and dP^T of block n: C tiles with column = this lane's query, rows = keys
+  auto sdp = [&](int n, f32x16& s, f32x16& dp) {
+    QB b = buf(n);
+    const T* krow = b.k + (l & 31) * LD + M::KW * h;
+    const T* vrow = b.v + (l & 31) * LD + M::KW * h;
+    s = zero16();
+    dp = zero16();
 #pragma unroll
-    for (int i = 0; i < PF; ++i) {
-      const int e = tid + i * NT;
-      const int r = e / CPR, c = (e - r * CPR) * VE;
-      const uint32_t off = (uint32_t)(kt * BK + r) * ROWB + c * sizeof(T);
-      if (KCH % NT == 0 || e < KCH) {
-        pk[i] = bload16<T>(rK, off);   // rows past the end read as zeros
-        pv[i] = bload16<T>(rV, off);
-      }
-    }
-    if constexpr (BF) {
-#pragma unroll
-      for (int i = 0; i < PFT; ++i) {
-        const int e = tid + i * NT;
-        const int cp = e % (HD / 2), rg = e / (HD / 2);
-        const uint32_t off = (uint32_t)(kt * BK + 4 * rg) * ROWB + cp * 4u;
-        if (KUN % NT == 0 || e < KUN) {
-#pragma unroll
-          for (int k = 0; k < 4; ++k) tk[i][k] = __float_as_uint(bload4(rK, off + k * ROWB));
-        }
-      }
+    for (int c = 0; c < NC; ++c) {
+      s = M::mma(ld_nat(krow + c * M::KD), qf[c], s);
+      dp = M::mma(ld_nat(vrow + c * M::KD), of[c], dp);
     }
   };
-  auto stage = [&]() {
+
+  // dS^T = p (dp - D) with p = 2^(s c - L log2 e); dQ^T += K^T.dS^T
+  auto finish = [&](auto masked, int n, f32x16 s, f32x16 dp) {
+    QB b = buf(n);
 #pragma unroll
-    for (int i = 0; i < PF; ++i) {
-      const int e = tid + i * NT;
-      if (KCH % NT == 0 || e < KCH) {
-        const int r = e / CPR, c = (e - r * CPR) * VE;
-        st16(Ks + r * LD + c, pk[i]);
-        st16(Vs + r * LD + c, pv[i]);
-      }
+    for (int v = 0; v < 16; ++v) {
+      const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[v], p.c_log2, -L2));
+      dp[v] = pr * (dp[v] - Di);
     }
-    if constexpr (BF) {
+    if constexpr (decltype(masked)::value) {
+      // key j is seen by query qi iff j <= qi
+      const int rel = qi - (n * NB + 4 * h);
 #pragma unroll
-      for (int i = 0; i < PFT; ++i) {
-        const int e = tid + i * NT;
-        if (KUN % NT == 0 || e < KUN) {
-          const int cp = e % (HD / 2), rg = e / (HD / 2);
-          put_t<TK>(reinterpret_cast<unsigned*>(KTs), 2 * cp, 4 * rg, tk[i]);
-        }
+      for (int v = 0; v < 16; ++v) dp[v] = (8 * (v >> 2) + (v & 3) > rel) ? 0.f : dp[v];
+    }
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const typename M::frag sf = frag_from_acc(dp, u, T{});
+#pragma unroll
+      for (int d = 0; d < NDB; ++d) {
+        typename M::frag af;
+        if constexpr (BF)
+          af = *reinterpret_cast<const bf16x8*>(b.kt + 2 * TB::chunk_dw(d * 32 + (l & 31), 2 * u + h));
+        else
+          af = ld_res(b.k, LD, 0, u, d * 32);
+        dqacc[d] = M::mma(af, sf, dqacc[d]);
       }
     }
   };
 
-  // one key tile: dQ update of this wave's queries
-  auto compute = [&](auto masked, int k0) {
-    f32x16 sacc[NKB], pacc[NKB];
+  // the compiler's own loads (qf, of, L, D) land before the staging loads start
+  settle(L2);
+  settle(Di);
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      sacc[kb] = zero16();
-      pacc[kb] = zero16();
-      const T* krow = Ks + (kb * 32 + (l & 31)) * LD + M::KW * h;
-      const T* vrow = Vs + (kb * 32 + (l & 31)) * LD + M::KW * h;
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        sacc[kb] = M::mma(ld_nat(krow + c * M::KD), qf[c], sacc[kb]);
-        pacc[kb] = M::mma(ld_nat(vrow + c * M::KD), of[c], pacc[kb]);
-      }
-    }
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      if constexpr (decltype(masked)::value) {
-        const int rel = key_lim - (k0 + kb * 32 + 4 * h);
-#pragma unroll
-        for (int v = 0; v < 16; ++v)
-          sacc[kb][v] = (8 * (v >> 2) + (v & 3) > rel) ? kNegInf : sacc[kb][v];
-      }
-      // p = 2^(s c - L log2 e) (0 where masked), dS^T = p (dp - D)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][v], p.c_log2, -L2));
-        pacc[kb][v] = pr * (pacc[kb][v] - Di);
-      }
-    }
-    // dQ^T += K^T . dS^T   (k runs over the tile's keys)
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-      for (int u = 0; u < NU; ++u) {
-        const typename M::frag sf = frag_from_acc(pacc[kb], u, T{});
-#pragma unroll
-        for (int d = 0; d < NDB; ++d) {
-          typename M::frag af;
-          if constexpr (BF)
-            af = *reinterpret_cast<const bf16x8*>(KTs + 2 * TK::chunk_dw(d * 32 + (l & 31), 4 * kb + 2 * u + h));
-          else
-            af = ld_res(Ks, LD, kb * 32, u, d * 32);
-          dqacc[d] = M::mma(af, sf, dqacc[d]);
-        }
-      }
-    }
-  };
-
-  // tiles before n_full are unmasked for every wave of the workgroup
-  const int n_full = min(p.causal ? (q0 + 1) / BK : n_tiles, S / BK);
-  auto step = [&](auto masked, int kt) {
+  for (int c = 0; c < NC; ++c) {
+    settle(qf[c]);
+    settle(of[c]);
+  }
+  f32x16 sa, pa, sb, pb;
+  load(a[0], 0);
+  wait_vm<0>(a[0].x);
+  put(a[0], 0);
+  load(a[0], 1);
+  wait_vm<0>(a[0].x);
+  put(a[0], 1);
+  load(a[0], 2);
+  load(a[1], 3);
+  __syncthreads();
+  sdp(0, sa, pa);
+  Pipe pipe(sa, pa, sb, pb);
+  auto body = [&](auto masked, auto par, int n) {
+    constexpr int P = decltype(par)::value;
+    wait_vm<NLOAD>(a[P].x);    // set P landed; set 1-P (one block behind) in flight
+    sdp(n + 1, pipe.next(par).s, pipe.next(par).dp);
+    put(a[P], n + 2);
+    finish(masked, n, pipe.cur(par).s, pipe.cur(par).dp);
+    load(a[P], n + 4);         // last: volatile loads order the memory accesses around them
     __syncthreads();
-    stage();
-    __syncthreads();
-    if (kt + 1 < n_tiles) prefetch(kt + 1);
-    const int k0 = kt * BK;
-    // the wave skips tiles wholly above its part of the diagonal
-    if (wave_live && !(p.causal && k0 > qw_last)) compute(masked, k0);
   };
-  prefetch(0);
-  for (int kt = 0; kt < n_full; ++kt) step(std::false_type{}, kt);
-  for (int kt = n_full; kt < n_tiles; ++kt) step(std::true_type{}, kt);
+  // causal: blocks [0, nm) are unmasked, nm = q0 / NB being a multiple of
+  // BQ / NB (even); non-causal: all are unmasked and there is no second run
+  int n = 0, par = 0;
+  pipe.run(body, std::false_type{}, n, min(nm, nl), par);
+  pipe.run(body, std::true_type{}, n, nl, par);
+  pipe.last(finish, nl >= nm, nl, par);
+  // drain the loads of blocks past the end; their registers stay reserved
+  // until the loads have landed
+  wait_vm<0>(a[0].x);
+  wait_vm<0>(a[1].x);
 
   // dQ_i (scaled): C tile column = query, rows = d
   const rsrc_t rdQ = make_rsrc(p.dQ + hoff, head_bytes);
@@ -529,7 +692,7 @@ __device__ __forceinline__ void query_role(const BwdParams<T>& p, int bh, int qq
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int dd = d * 32 + 8 * g + 4 * h;
-      if (HDP == HD || dd < HD) store4<T>(rdQ, qrow + dd * sizeof(T), dqacc[d], g, p.scale);
+      if (G::HDP == HD || dd < HD) store4<T>(rdQ, qrow + dd * sizeof(T), dqacc[d], g, p.scale);
     }
   }
 }
@@ -538,13 +701,9 @@ __device__ __forceinline__ void query_role(const BwdParams<T>& p, int bh, int qq
 template <typename T, int HD>
 struct BwdCfg {
   static constexpr int NW = 4;
-  // query tile of the key workgroups (fp32 tiles at hd >= 64 are halved to fit LDS)
-  static constexpr int BQ = (sizeof(T) == 4 && HD >= 64) ? 32 : 64;
-  // key tile of the query workgroups
-  static constexpr int BK = 64;
-  static constexpr size_t SMEM = KeyTiles<T, HD, NW, BQ>::BYTES > QueryTiles<T, HD, NW, BK>::BYTES
-                                     ? KeyTiles<T, HD, NW, BQ>::BYTES
-                                     : QueryTiles<T, HD, NW, BK>::BYTES;
+  static constexpr size_t KEY_BYTES = 3 * KeyBuf<T, HD, NW>::BYTES;
+  static constexpr size_t QUERY_BYTES = 3 * QueryBuf<T, HD, NW>::BYTES;
+  static constexpr size_t SMEM = KEY_BYTES > QUERY_BYTES ? KEY_BYTES : QUERY_BYTES;
 };
 
 // Per head: nkt key workgroups (heaviest first: the earliest keys see the
@@ -559,8 +718,8 @@ __global__ __launch_bounds__((BwdCfg<T, HD>::NW * 64), 1) void bwd_kernel(BwdPar
   const int lid = xcd_logical(blockIdx.x, nwg);
   const int bh = lid / per_head;
   const int r = lid - bh * per_head;
-  if (r < nkt) key_role<T, HD, C::NW, C::BQ>(p, bh, r, smem);
-  else query_role<T, HD, C::NW, C::BK>(p, bh, nqq - 1 - (r - nkt), smem);
+  if (r < nkt) key_role<T, HD, C::NW>(p, bh, r, smem);
+  else query_role<T, HD, C::NW>(p, bh, nqq - 1 - (r - nkt), smem);
 }
 
 template <typename T, int HD>
