@@ -168,8 +168,7 @@ __device__ inline void settle(X& x) {
 }
 
 // Staging of one block of two tensors A and B ([S][HD] rows row0..row0+31) in
-// 4-row x 1-chunk units, rows fastest across lanes: unit u of a tensor covers
-// rows 4*(u % 8) .. +3 and chunk u / 8.  The first NW/2 waves stage A and
+// 4-row x 1-chunk units, rows fastest across lanes (see chunk()).  The first NW/2 waves stage A and
 // the others B, so the tensor is wave-uniform.  Every thread issues exactly
 // NLOAD loads per block (threads without a unit read past the buffer end,
 // which returns zeros), so all waves count the same loads in flight.  A (B)
@@ -184,6 +183,16 @@ struct Stage2 {
 
   __device__ static inline bool wave_a() { return __builtin_amdgcn_readfirstlane((int)threadIdx.x) < HALF; }
   __device__ static inline int unit(int i) { return (int)(threadIdx.x % HALF) + i * HALF; }
+  // unit u covers rows 4 * (u % 8) .. +3 and 16-byte chunk chunk(u): the
+  // chunks of eight consecutive units are rotated by two for the upper four
+  // row groups, which spreads the row-major writes of a 16-lane pass over all
+  // banks (row stride LD = 4 mod 16 dwords); the transposed writes stay
+  // conflict-free with it
+  static constexpr int J = G::CPR < 8 ? G::CPR : 8;
+  __device__ static inline int chunk(int u) {
+    const int j = (u >> 3) % J, hi = (u >> 3) / J;
+    return (j + 2 * ((u & 7) >> 2)) % J + J * hi;
+  }
 
   __device__ inline void load(const u32x4s& da, const u32x4s& db, int row0) {
     const u32x4s d = wave_a() ? da : db;
@@ -191,7 +200,7 @@ struct Stage2 {
     for (int i = 0; i < PFU; ++i) {
       const int u = unit(i);
       const uint32_t off = (G::UPT % HALF == 0 || u < G::UPT)
-                               ? (uint32_t)(row0 + 4 * (u & 7)) * G::ROWB + (uint32_t)(u >> 3) * 16u
+                               ? (uint32_t)(row0 + 4 * (u & 7)) * G::ROWB + (uint32_t)chunk(u) * 16u
                                : 0x80000000u;
 #pragma unroll
       for (int k = 0; k < 4; ++k) x[i][k] = asm_load16(d, off + k * G::ROWB);
@@ -210,7 +219,7 @@ struct Stage2 {
     for (int i = 0; i < PFU; ++i) {
       const int u = unit(i);
       if (G::UPT % HALF == 0 || u < G::UPT) {
-        const int r = 4 * (u & 7), c = (u >> 3) * G::VE;
+        const int r = 4 * (u & 7), c = chunk(u) * G::VE;
         T* dst = (is_a ? a : b) + r * G::LD + c;
 #pragma unroll
         for (int k = 0; k < 4; ++k) *reinterpret_cast<u32x4*>(dst + k * G::LD) = x[i][k];
