@@ -212,6 +212,26 @@ struct Stage2 {
 #pragma unroll
       for (int k = 0; k < 4; ++k) settle(x[i][k]);
   }
+  // Part k (0..3) of store(): row k of each unit row-major and column pair
+  // k transposed, so the writes can be spread between other work.
+  __device__ inline void store_part(int k, T* a, T* b, T* at, T* bt) const {
+    const bool is_a = wave_a();
+#pragma unroll
+    for (int i = 0; i < PFU; ++i) {
+      const int u = unit(i);
+      if (G::UPT % HALF == 0 || u < G::UPT) {
+        const int r = 4 * (u & 7), c = chunk(u) * G::VE;
+        T* dst = (is_a ? a : b) + r * G::LD + c;
+        *reinterpret_cast<u32x4*>(dst + k * G::LD) = x[i][k];
+        if constexpr ((TRA || TRB) && G::BF) {
+          if ((TRA && is_a) || (TRB && !is_a)) {
+            const unsigned col[4] = {x[i][0][k], x[i][1][k], x[i][2][k], x[i][3][k]};
+            put_t(reinterpret_cast<unsigned*>(is_a ? at : bt), c + 2 * k, r, col);
+          }
+        }
+      }
+    }
+  }
   // a, b: row-major blocks (row stride LD); at, bt: their transposed blocks
   __device__ inline void store(T* a, T* b, T* at, T* bt) const {
     const bool is_a = wave_a();
@@ -331,7 +351,7 @@ __device__ __forceinline__ void key_role(const BwdParams<T>& p, int bh, int kt, 
   constexpr int NB = G::NB, NDB = G::NDB, NC = G::NC, NU = G::NU, LD = G::LD;
   constexpr uint32_t ROWB = G::ROWB;
   constexpr int BKV = NW * 32;
-  static_assert(NB <= G::NT, "L/D staging assumes one thread per query");
+  static_assert(NB == 32, "L/D staging: lanes 0..31 hold L, lanes 32..63 hold D");
   static_assert((BKV / NB) % 2 == 0, "the diagonal run must have an even length");
 
   const int S = p.S;
@@ -466,10 +486,10 @@ __device__ __forceinline__ void key_role(const BwdParams<T>& p, int bh, int kt, 
   auto put = [&](const Staged& z, int n) {
     KB b = buf(n);
     z.x.store(b.q, b.dO, b.qt, b.dOt);
-    if (tid < NB) {
-      b.L[tid] = z.l * kLog2e;   // L in log2 units (the load has landed: see ready())
-      b.D[tid] = z.d;
-    }
+    // lanes 0..31 write L (log2 units) and lanes 32..63 write D of row
+    // lane % 32; every wave writes the same values, which keeps the store
+    // free of branches (a branch would split the scheduling region)
+    b.L[l] = (l < NB) ? z.l * kLog2e : z.d;
   };
 
   // the compiler's own loads (kf, vf) land before the staging loads start
@@ -490,14 +510,97 @@ __device__ __forceinline__ void key_role(const BwdParams<T>& p, int bh, int kt, 
   __syncthreads();
   sdp(n0, sa, pa);
   Pipe pipe(sa, pa, sb, pb);
+  // bf16 iteration with the work interleaved by hand (sched_barrier fences
+  // keep the order): the score contractions of block n+1 alternate with the
+  // exponentials and dS of block n, and the gradient contractions of block n
+  // with the staging writes of block n+2.  Same arithmetic as sdp() then
+  // finish().
+  auto fused = [&](auto masked, auto par, int n) {
+    if constexpr (BF) {
+      constexpr int P = decltype(par)::value;
+      constexpr int EPC = (16 + NC - 1) / NC;    // score elements finished per contraction step
+      ready(One{}, a[P]);        // set P landed; set 1-P (one block behind) in flight
+      KB bn = buf(n + 1), bc = buf(n), bs = buf(n + 2);
+      f32x16& sn = pipe.next(par).s;
+      f32x16& dn = pipe.next(par).dp;
+      f32x16 s = pipe.cur(par).s, dp = pipe.cur(par).dp;
+      typename M::frag qa[NC], oa[NC];
+      const T* qrow = bn.q + (l & 31) * LD + M::KW * h;
+      const T* orow = bn.dO + (l & 31) * LD + M::KW * h;
+  #pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        qa[c] = ld_nat(qrow + c * M::KD);
+        oa[c] = ld_nat(orow + c * M::KD);
+      }
+      f32x4 L4[4], D4[4];
+  #pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        L4[g] = *reinterpret_cast<const f32x4*>(bc.L + 8 * g + 4 * h);
+        D4[g] = *reinterpret_cast<const f32x4*>(bc.D + 8 * g + 4 * h);
+      }
+      const int lo = kj - (n * NB + 4 * h);      // masked: query row rel sees key kj iff rel >= lo
+      sn = zero16();
+      dn = zero16();
+  #pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        __builtin_amdgcn_sched_barrier(0);
+        sn = M::mma(qa[c], kf[c], sn);
+        dn = M::mma(oa[c], vf[c], dn);
+  #pragma unroll
+        for (int v = c * EPC; v < (c + 1) * EPC && v < 16; ++v) {
+          const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[v], p.c_log2, -L4[v >> 2][v & 3]));
+          float ps = pr, ds = pr * (dp[v] - D4[v >> 2][v & 3]);
+          if constexpr (decltype(masked)::value) {
+            const bool keep = 8 * (v >> 2) + (v & 3) >= lo;
+            ps = keep ? ps : 0.f;
+            ds = keep ? ds : 0.f;
+          }
+          s[v] = ps;
+          dp[v] = ds;
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      typename M::frag pf[NU], sf[NU], ta[NU][NDB], tb[NU][NDB];
+  #pragma unroll
+      for (int u = 0; u < NU; ++u) {
+        pf[u] = frag_from_acc(s, u, T{});
+        sf[u] = frag_from_acc(dp, u, T{});
+  #pragma unroll
+        for (int d = 0; d < NDB; ++d) {
+          const int c = d * 32 + (l & 31);
+          ta[u][d] = *reinterpret_cast<const bf16x8*>(bc.dOt + 2 * TB::chunk_dw(c, 2 * u + h));
+          tb[u][d] = *reinterpret_cast<const bf16x8*>(bc.qt + 2 * TB::chunk_dw(c, 2 * u + h));
+        }
+      }
+      constexpr int NG = NU * NDB;               // gradient contraction pairs
+  #pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        __builtin_amdgcn_sched_barrier(0);
+        const int u = g / NDB, d = g % NDB;
+        dvacc[d] = M::mma(ta[u][d], pf[u], dvacc[d]);
+        dkacc[d] = M::mma(tb[u][d], sf[u], dkacc[d]);
+        // the four store parts spread over the NG steps
+#pragma unroll
+        for (int k = g * 4 / NG; k < (g + 1) * 4 / NG; ++k) a[P].x.store_part(k, bs.q, bs.dO, bs.qt, bs.dOt);
+        if (g == 0) bs.L[l] = (l < NB) ? a[P].l * kLog2e : a[P].d;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      load(a[P], n + 4);         // last: volatile loads order the memory accesses around them
+      __syncthreads();
+    }
+  };
   auto body = [&](auto masked, auto par, int n) {
-    constexpr int P = decltype(par)::value;
-    ready(One{}, a[P]);        // set P landed; set 1-P (one block behind) in flight
-    sdp(n + 1, pipe.next(par).s, pipe.next(par).dp);
-    put(a[P], n + 2);
-    finish(masked, n, pipe.cur(par).s, pipe.cur(par).dp);
-    load(a[P], n + 4);         // last: volatile loads order the memory accesses around them
-    __syncthreads();
+    if constexpr (BF) {
+      fused(masked, par, n);
+    } else {
+      constexpr int P = decltype(par)::value;
+      ready(One{}, a[P]);      // set P landed; set 1-P (one block behind) in flight
+      sdp(n + 1, pipe.next(par).s, pipe.next(par).dp);
+      put(a[P], n + 2);
+      finish(masked, n, pipe.cur(par).s, pipe.cur(par).dp);
+      load(a[P], n + 4);       // last: volatile loads order the memory accesses around them
+      __syncthreads();
+    }
   };
   // causal: the first BKV/NB blocks cross the diagonal (an even count), or
   // all of them if fewer remain; non-causal: none
