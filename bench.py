@@ -38,7 +38,7 @@ KERNEL_SRC = {
     "fwd": "transformer_attention_xfa_amd/csrc/xfa_fwd.hip",
     "pre": "transformer_attention_xfa_amd/csrc/xfa_pre.hip",
 }
-KERNEL_NAME = {"fwd": "fwd_kernel", "pre": "bwd_pre_kernel", "bwd": "bwd_kernel"}
+KERNEL_NAME = {"fwd": "fwd_kernel", "pre": "bwd_pre_kernel", "bwd": "bwd_key_kernel + bwd_query_kernel"}
 
 
 def source_digest(phase: str) -> str:

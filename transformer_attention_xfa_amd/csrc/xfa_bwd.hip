@@ -8,7 +8,7 @@
 // Work split.  The page's kernel looped over query rows and added dK/dV into
 // global memory with atomics, which it names as its bottleneck; its own
 // follow-up is a key-block-owned dK/dV pass (Key Design Decisions, escape
-// hatches).  Here one launch holds two kinds of workgroups, each owning its
+// hatches).  Here two kinds of workgroups (two launches) each own their
 // outputs outright, so nothing is summed across workgroups:
 //   * key workgroups, one per (head, 32*NW keys): wave w keeps dK and dV of
 //     its 32 keys in registers and sweeps the 32-query blocks from the
@@ -24,14 +24,16 @@
 // workspace, and dQ is bitwise reproducible.
 //
 // Pipeline.  The streamed 32-row blocks (Q, dO, L, D for a key workgroup;
-// K, V for a query workgroup) rotate through three LDS buffers.  Iteration n
+// K, V for a query workgroup) rotate through three LDS buffers, and two
+// staged blocks are in flight in registers, so a global load has more than an
+// iteration to land.  In a key workgroup (one wave per SIMD), iteration n
 // (one workgroup barrier) forms the two score contractions of block n+1,
-// writes block n+2 from registers into the buffer block n-1 used, finishes
-// block n (exponentials, dS and the gradient contractions) and issues the
-// global loads of block n+4: two staged blocks are in flight in registers,
-// so a load has more than an iteration to land.  The score contractions of
-// n+1 do not depend on block n's exponentials, so the matrix cores have work
-// while the vector units evaluate them.
+// writes block n+2 into the buffer block n-1 used, finishes block n
+// (exponentials, dS and the gradient contractions) and issues the loads of
+// block n+4; the score contractions of n+1 do not depend on block n's
+// exponentials, so the matrix cores have work while the vector units
+// evaluate them.  A query workgroup runs two waves per SIMD instead and
+// finishes each block in its own iteration.
 //
 // For bf16 the operands whose contraction index runs along block rows (dO^T,
 // Q^T for the key workgroups, K^T for the query workgroups) are also written
@@ -296,7 +298,7 @@ struct Pipe {
   // parity P the staged set P was always issued before set 1-P, which is
   // what the body's wait count relies on.
   template <typename Body, typename Masked>
-  __device__ void run(Body& body, Masked m, int& n, int end, int& par) {
+  __device__ static void run(Body& body, Masked m, int& n, int end, int& par) {
     using P0 = std::integral_constant<int, 0>;
     using P1 = std::integral_constant<int, 1>;
     if (n >= end) return;
@@ -764,7 +766,9 @@ __device__ __forceinline__ void query_role(const BwdParams<T>& p, int bh, int qq
     settle(qf[c]);
     settle(of[c]);
   }
-  f32x16 sa, pa, sb, pb;
+  // One block per iteration, score and gradient contractions back to back:
+  // this kernel runs two waves per SIMD (it fits in half the register
+  // file), and the other wave's work overlaps each wave's waits.
   load(a[0], 0);
   wait_vm<0>(a[0].x);
   put(a[0], 0);
@@ -774,23 +778,27 @@ __device__ __forceinline__ void query_role(const BwdParams<T>& p, int bh, int qq
   load(a[0], 2);
   load(a[1], 3);
   __syncthreads();
-  sdp(0, sa, pa);
-  Pipe pipe(sa, pa, sb, pb);
   auto body = [&](auto masked, auto par, int n) {
     constexpr int P = decltype(par)::value;
+    f32x16 s, dp;
+    sdp(n, s, dp);
     wait_vm<NLOAD>(a[P].x);    // set P landed; set 1-P (one block behind) in flight
-    sdp(n + 1, pipe.next(par).s, pipe.next(par).dp);
     put(a[P], n + 2);
-    finish(masked, n, pipe.cur(par).s, pipe.cur(par).dp);
+    finish(masked, n, s, dp);
     load(a[P], n + 4);         // last: volatile loads order the memory accesses around them
     __syncthreads();
   };
   // causal: blocks [0, nm) are unmasked, nm = q0 / NB being a multiple of
   // BQ / NB (even); non-causal: all are unmasked and there is no second run
   int n = 0, par = 0;
-  pipe.run(body, std::false_type{}, n, min(nm, nl), par);
-  pipe.run(body, std::true_type{}, n, nl, par);
-  pipe.last(finish, nl >= nm, nl, par);
+  Pipe::run(body, std::false_type{}, n, min(nm, nl), par);
+  Pipe::run(body, std::true_type{}, n, nl, par);
+  {
+    f32x16 s, dp;
+    sdp(nl, s, dp);
+    if (nl >= nm) finish(std::true_type{}, nl, s, dp);
+    else finish(std::false_type{}, nl, s, dp);
+  }
   // drain the loads of blocks past the end; their registers stay reserved
   // until the loads have landed
   wait_vm<0>(a[0].x);
@@ -818,20 +826,27 @@ struct BwdCfg {
   static constexpr size_t SMEM = KEY_BYTES > QUERY_BYTES ? KEY_BYTES : QUERY_BYTES;
 };
 
-// Per head: nkt key workgroups (heaviest first: the earliest keys see the
-// most queries), then nqq query workgroups (heaviest first: the last queries
-// see the most keys).  One head's workgroups stay on one XCD.
+// Two launches on the caller's stream.  Key workgroups (heaviest first: the
+// earliest keys see the most queries) need the whole register file, one wave
+// per SIMD; query workgroups (heaviest first: the last queries see the most
+// keys) fit two waves per SIMD for bf16.  A head's workgroups stay on one XCD.
 template <typename T, int HD>
-__global__ __launch_bounds__((BwdCfg<T, HD>::NW * 64), 1) void bwd_kernel(BwdParams<T> p, int nkt, int nqq,
-                                                                         int nwg) {
+__global__ __launch_bounds__((BwdCfg<T, HD>::NW * 64), 1) void bwd_key_kernel(BwdParams<T> p, int nkt, int nwg) {
   using C = BwdCfg<T, HD>;
-  __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
-  const int per_head = nkt + nqq;
+  __shared__ __attribute__((aligned(16))) char smem[C::KEY_BYTES];
   const int lid = xcd_logical(blockIdx.x, nwg);
-  const int bh = lid / per_head;
-  const int r = lid - bh * per_head;
-  if (r < nkt) key_role<T, HD, C::NW>(p, bh, r, smem);
-  else query_role<T, HD, C::NW>(p, bh, nqq - 1 - (r - nkt), smem);
+  const int bh = lid / nkt;
+  key_role<T, HD, C::NW>(p, bh, lid - bh * nkt, smem);
+}
+
+template <typename T, int HD>
+__global__ __launch_bounds__((BwdCfg<T, HD>::NW * 64), (sizeof(T) == 2 ? 2 : 1)) void bwd_query_kernel(
+    BwdParams<T> p, int nqq, int nwg) {
+  using C = BwdCfg<T, HD>;
+  __shared__ __attribute__((aligned(16))) char smem[C::QUERY_BYTES];
+  const int lid = xcd_logical(blockIdx.x, nwg);
+  const int bh = lid / nqq;
+  query_role<T, HD, C::NW>(p, bh, nqq - 1 - (lid - bh * nqq), smem);
 }
 
 template <typename T, int HD>
@@ -841,10 +856,13 @@ static hipError_t launch_bwd_t(const BwdArgs& a) {
   constexpr int BQQ = C::NW * 32;                // queries per query workgroup
   const int nkt = (int)((a.S + BKV - 1) / BKV);
   const int nqq = (int)((a.S + BQQ - 1) / BQQ);
-  const int nwg = (int)(a.BH * (nkt + nqq));
   BwdParams<T> p{(const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.dout, a.lse, a.delta,
                  (T*)a.dq, (T*)a.dk, (T*)a.dv, (int)a.S, a.scale, a.scale * kLog2e, a.causal};
-  hipLaunchKernelGGL((bwd_kernel<T, HD>), dim3(nwg), dim3(C::NW * 64), 0, a.stream, p, nkt, nqq, nwg);
+  const int nk = (int)(a.BH * nkt), nq = (int)(a.BH * nqq);
+  hipLaunchKernelGGL((bwd_key_kernel<T, HD>), dim3(nk), dim3(C::NW * 64), 0, a.stream, p, nkt, nk);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_query_kernel<T, HD>), dim3(nq), dim3(C::NW * 64), 0, a.stream, p, nqq, nq);
   return hipGetLastError();
 }
 
