@@ -89,8 +89,10 @@ xfa_status_t xfa_bwd_preprocess(const void* out, const void* dout, float* delta,
  *   in : q, k, v, dout [B,H,S,hd] dtype; lse [B,H,S] from xfa_fwd;
  *        delta [B,H,S] from xfa_bwd_preprocess
  *   out: dq, dk, dv    [B,H,S,hd] dtype (fully overwritten)
- * One kernel, no scratch memory.  Each output element is produced by exactly
- * one workgroup (no atomics), so results are bitwise reproducible.           */
+ * Two kernels on `stream` (dK/dV, then dQ), no scratch memory.  Each output
+ * element is produced by exactly one workgroup (no atomics), so results are
+ * bitwise reproducible.  On XFA_ERR_HIP the dK/dV kernel may have been
+ * enqueued already; the outputs are then unspecified.                        */
 xfa_status_t xfa_bwd(const void* q, const void* k, const void* v, const void* dout,
                      const float* lse, const float* delta, void* dq, void* dk, void* dv,
                      int64_t B, int64_t H, int64_t S, int64_t hd, float scale, int causal,
