@@ -48,6 +48,7 @@
 
 #include "xfa_common.h"
 #include "xfa_launch.h"
+#include "xfa_stage.h"
 
 namespace xfa {
 
@@ -59,279 +60,12 @@ struct BwdParams {
   int S; float scale; float c_log2; int causal;
 };
 
-// Geometry shared by both workgroup kinds: streamed blocks of NB = 32 rows.
-template <typename T, int HD, int NW>
-struct BwdGeo {
-  using M = Mma<T>;
-  static constexpr bool BF = sizeof(T) == 2;
-  static constexpr int NB = 32;
-  static constexpr int NT = NW * 64;
-  static constexpr int HDP = HD < 32 ? 32 : HD;
-  static constexpr int NDB = HDP / 32;           // 32-row d blocks
-  static constexpr int NC = HD / M::KD;          // instructions along d
-  static constexpr int NU = 32 / M::KD;          // instructions per 32-wide k block
-  static constexpr int VE = Vec16<T>::N;
-  static constexpr int CPR = HD / VE;            // 16-byte chunks per row
-  static constexpr int UPT = (NB / 4) * CPR;     // 4-row x 1-chunk units per block of a tensor
-  static constexpr int PFU = (2 * UPT + NT - 1) / NT;   // units per thread (two tensors)
-  // row-major tiles: a row stride of 4 (mod 8) dwords reads conflict-free
-  static constexpr int LD = HDP + (BF ? 8 : 4);
-  static constexpr int NE = NB * LD;             // elements of a row-major block
-  static constexpr int TE = BF ? HDP * NB : 0;   // elements of a transposed block
-  static constexpr uint32_t ROWB = HD * sizeof(T);
-  static_assert(HD % M::KD == 0 && HD % VE == 0, "unsupported head dim");
-};
-using TB = TTile<32>;
-
-// Four rows x two bf16 columns of a block -> the transposed block.
-__device__ inline void put_t(unsigned* t, int c, int r, const unsigned x[4]) {
-  u32x2 col0, col1;
-  transpose_4x2(x, col0, col1);
-  const int p = swap23(r);
-  const bool odd_first = (lane() >> 3) & 1;
-  const int c_first = c + (odd_first ? 1 : 0);
-  const int dw_half = 2 * ((p >> 2) & 1);
-  *reinterpret_cast<u32x2*>(t + TB::chunk_dw(c_first, p >> 3) + dw_half) = odd_first ? col1 : col0;
-  *reinterpret_cast<u32x2*>(t + TB::chunk_dw(c_first ^ 1, p >> 3) + dw_half) = odd_first ? col0 : col1;
-}
-
-// Global loads of the streamed blocks are issued through inline assembly and
-// waited for explicitly: the compiler's own wait-count placement merges the
-// states of the unrolled loop bodies conservatively and then waits for every
-// load in flight, including the ones issued just before, which exposes the
-// full load latency once per iteration.  These loads are the only vector
-// memory operations inside the loops; every load the compiler issues itself
-// (the per-lane K/V or Q/dO rows) has been waited for before the first of
-// them (see settle()).  The compiler takes an asm load's result register as
-// written when the instruction issues, so every such register is kept live
-// (used by a settle() after the matching wait) until its load has landed;
-// otherwise it could hand the register to another value that the late load
-// data would then overwrite.
-typedef unsigned u32x4s __attribute__((ext_vector_type(4)));
-
-// A raw buffer descriptor in scalar registers: 48-bit base, no stride,
-// nbytes records, 32-bit raw data (same fields make_buffer_rsrc produces).
-__device__ inline u32x4s make_desc(const void* base, uint32_t nbytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  return u32x4s{(unsigned)__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
-                (unsigned)__builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu)),
-                (unsigned)__builtin_amdgcn_readfirstlane((int)nbytes), (unsigned)kRsrcWord3};
-}
-// The loads are volatile (never removed, duplicated or moved across another
-// volatile statement or memory access), so the count of loads issued after a
-// set is exactly what the code says; a load's result is only read through the
-// wait that covers it (wait_vm with the registers as operands).
-__device__ inline u32x4 asm_load16(const u32x4s& d, uint32_t off) {
-  u32x4 r;
-  asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen" : "=v"(r) : "v"(off), "s"(d));
-  return r;
-}
-__device__ inline float asm_load4(const u32x4s& d, uint32_t off) {
-  float r;
-  asm volatile("buffer_load_dword %0, %1, %2, 0 offen" : "=v"(r) : "v"(off), "s"(d));
-  return r;
-}
-// Wait until at most N of this wave's vector memory operations are in flight.
-template <int N>
-__device__ inline void wait_vm() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N));
-}
-// The same wait, also marking the registers of the loads it covers as
-// (re)defined by it, so that no use of them can move above it.
-template <int N>
-__device__ inline void wait_vm(u32x4 (&x)[1][4]) {
-  asm volatile("s_waitcnt vmcnt(%4)" : "+v"(x[0][0]), "+v"(x[0][1]), "+v"(x[0][2]), "+v"(x[0][3]) : "n"(N));
-}
-template <int N>
-__device__ inline void wait_vm(u32x4 (&x)[2][4]) {
-  asm volatile("s_waitcnt vmcnt(%8)"
-               : "+v"(x[0][0]), "+v"(x[0][1]), "+v"(x[0][2]), "+v"(x[0][3]), "+v"(x[1][0]), "+v"(x[1][1]),
-                 "+v"(x[1][2]), "+v"(x[1][3])
-               : "n"(N));
-}
-template <int N>
-__device__ inline void wait_vm(u32x4 (&x)[1][4], float& a, float& b) {
-  asm volatile("s_waitcnt vmcnt(%6)"
-               : "+v"(x[0][0]), "+v"(x[0][1]), "+v"(x[0][2]), "+v"(x[0][3]), "+v"(a), "+v"(b)
-               : "n"(N));
-}
-template <int N>
-__device__ inline void wait_vm(u32x4 (&x)[2][4], float& a, float& b) {
-  asm volatile("s_waitcnt vmcnt(%10)"
-               : "+v"(x[0][0]), "+v"(x[0][1]), "+v"(x[0][2]), "+v"(x[0][3]), "+v"(x[1][0]), "+v"(x[1][1]),
-                 "+v"(x[1][2]), "+v"(x[1][3]), "+v"(a), "+v"(b)
-               : "n"(N));
-}
-// Mark a register as (re)defined here, after the preceding wait: uses of it
-// cannot move above this point.
-template <typename X>
-__device__ inline void settle(X& x) {
-  asm volatile("" : "+v"(x));
-}
-
-// Staging of one block of two tensors A and B ([S][HD] rows row0..row0+31) in
-// 4-row x 1-chunk units, rows fastest across lanes (see chunk()).  The first NW/2 waves stage A and
-// the others B, so the tensor is wave-uniform.  Every thread issues exactly
-// NLOAD loads per block (threads without a unit read past the buffer end,
-// which returns zeros), so all waves count the same loads in flight.  A (B)
-// is also written transposed when TRA (TRB) is set (bf16 only).
-template <typename T, int HD, int NW, bool TRA, bool TRB>
-struct Stage2 {
-  using G = BwdGeo<T, HD, NW>;
-  static constexpr int HALF = G::NT / 2;                   // threads per tensor
-  static constexpr int PFU = (G::UPT + HALF - 1) / HALF;   // units per thread
-  static constexpr int NLOAD = 4 * PFU;
-  u32x4 x[PFU][4];
-
-  __device__ static inline bool wave_a() { return __builtin_amdgcn_readfirstlane((int)threadIdx.x) < HALF; }
-  __device__ static inline int unit(int i) { return (int)(threadIdx.x % HALF) + i * HALF; }
-  // unit u covers rows 4 * (u % 8) .. +3 and 16-byte chunk chunk(u): the
-  // chunks of eight consecutive units are rotated by two for the upper four
-  // row groups, which spreads the row-major writes of a 16-lane pass over all
-  // banks (row stride LD = 4 mod 16 dwords); the transposed writes stay
-  // conflict-free with it
-  static constexpr int J = G::CPR < 8 ? G::CPR : 8;
-  __device__ static inline int chunk(int u) {
-    const int j = (u >> 3) % J, hi = (u >> 3) / J;
-    return (j + 2 * ((u & 7) >> 2)) % J + J * hi;
-  }
-
-  __device__ inline void load(const u32x4s& da, const u32x4s& db, int row0) {
-    const u32x4s d = wave_a() ? da : db;
-#pragma unroll
-    for (int i = 0; i < PFU; ++i) {
-      const int u = unit(i);
-      const uint32_t off = (G::UPT % HALF == 0 || u < G::UPT)
-                               ? (uint32_t)(row0 + 4 * (u & 7)) * G::ROWB + (uint32_t)chunk(u) * 16u
-                               : 0x80000000u;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) x[i][k] = asm_load16(d, off + k * G::ROWB);
-    }
-  }
-  __device__ inline void settle_all() {
-#pragma unroll
-    for (int i = 0; i < PFU; ++i)
-#pragma unroll
-      for (int k = 0; k < 4; ++k) settle(x[i][k]);
-  }
-  // Part k (0..3) of store(): row k of each unit row-major and column pair
-  // k transposed, so the writes can be spread between other work.
-  __device__ inline void store_part(int k, T* a, T* b, T* at, T* bt) const {
-    const bool is_a = wave_a();
-#pragma unroll
-    for (int i = 0; i < PFU; ++i) {
-      const int u = unit(i);
-      if (G::UPT % HALF == 0 || u < G::UPT) {
-        const int r = 4 * (u & 7), c = chunk(u) * G::VE;
-        T* dst = (is_a ? a : b) + r * G::LD + c;
-        *reinterpret_cast<u32x4*>(dst + k * G::LD) = x[i][k];
-        if constexpr ((TRA || TRB) && G::BF) {
-          if ((TRA && is_a) || (TRB && !is_a)) {
-            const unsigned col[4] = {x[i][0][k], x[i][1][k], x[i][2][k], x[i][3][k]};
-            put_t(reinterpret_cast<unsigned*>(is_a ? at : bt), c + 2 * k, r, col);
-          }
-        }
-      }
-    }
-  }
-  // a, b: row-major blocks (row stride LD); at, bt: their transposed blocks
-  __device__ inline void store(T* a, T* b, T* at, T* bt) const {
-    const bool is_a = wave_a();
-#pragma unroll
-    for (int i = 0; i < PFU; ++i) {
-      const int u = unit(i);
-      if (G::UPT % HALF == 0 || u < G::UPT) {
-        const int r = 4 * (u & 7), c = chunk(u) * G::VE;
-        T* dst = (is_a ? a : b) + r * G::LD + c;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) *reinterpret_cast<u32x4*>(dst + k * G::LD) = x[i][k];
-        if constexpr ((TRA || TRB) && G::BF) {
-          if ((TRA && is_a) || (TRB && !is_a)) {
-            unsigned* t = reinterpret_cast<unsigned*>(is_a ? at : bt);
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-              const unsigned col[4] = {x[i][0][m], x[i][1][m], x[i][2][m], x[i][3][m]};
-              put_t(t, c + 2 * m, r, col);
-            }
-          }
-        }
-      }
-    }
-  }
-};
-
-// Four consecutive C-tile results, scaled, to one row of an output tensor.
-template <typename T>
-__device__ inline void store4(rsrc_t r, uint32_t off, const f32x16& a, int g, float s) {
-  bstore_row4(r, off, a[4 * g] * s, a[4 * g + 1] * s, a[4 * g + 2] * s, a[4 * g + 3] * s, T{});
-}
-
-// Zero the d >= HD padding of the blocks (hd = 16 only); padded rows and
-// columns feed only C-tile rows that are never stored.
-template <typename T, int HD, int NW>
-__device__ inline void zero_pad(T* nat, T* tr) {
-  using G = BwdGeo<T, HD, NW>;
-  if constexpr (G::HDP != HD) {
-    for (int e = threadIdx.x; e < G::NB * (G::HDP - HD); e += G::NT) {
-      const int r = e / (G::HDP - HD), c = HD + e % (G::HDP - HD);
-      nat[r * G::LD + c] = (T)0.f;
-    }
-    if constexpr (G::BF)
-      for (int e = threadIdx.x; e < (G::HDP - HD) * G::NB; e += G::NT) tr[HD * G::NB + e] = (T)0.f;
-  }
-}
-
-// Two sets of score tiles alternate between "block n being finished" and
-// "block n+1 being formed"; which set plays which part is the iteration's
-// parity, a compile-time constant in every loop body (loops are unrolled by
-// two by hand: the workgroup barrier in the body keeps the compiler from
-// unrolling them itself), so no tile is ever copied.
-struct Pipe {
-  struct Pair { f32x16& s; f32x16& dp; };
-  Pair p0, p1;
-  __device__ Pipe(f32x16& s0, f32x16& d0, f32x16& s1, f32x16& d1) : p0{s0, d0}, p1{s1, d1} {}
-  template <int P> __device__ Pair cur(std::integral_constant<int, P>) { return P ? p1 : p0; }
-  template <int P> __device__ Pair next(std::integral_constant<int, P>) { return P ? p0 : p1; }
-  // Iterations [n, end) of body(masked, parity, n), starting at parity 0;
-  // par becomes the parity after them.  Callers start a run only at parity 0
-  // (every run but the last has an even length), so at the entry of a body of
-  // parity P the staged set P was always issued before set 1-P, which is
-  // what the body's wait count relies on.
-  template <typename Body, typename Masked>
-  __device__ static void run(Body& body, Masked m, int& n, int end, int& par) {
-    using P0 = std::integral_constant<int, 0>;
-    using P1 = std::integral_constant<int, 1>;
-    if (n >= end) return;
-    for (; n + 1 < end; n += 2) {
-      body(m, P0{}, n);
-      body(m, P1{}, n + 1);
-    }
-    par = 0;
-    if (n < end) {
-      body(m, P0{}, n);
-      ++n;
-      par = 1;
-    }
-  }
-  // the final block: finish(masked, n, s, dp) without a successor
-  template <typename Finish>
-  __device__ void last(Finish& finish, bool masked, int n, int par) {
-    if (par) {
-      if (masked) finish(std::true_type{}, n, p1.s, p1.dp);
-      else finish(std::false_type{}, n, p1.s, p1.dp);
-    } else {
-      if (masked) finish(std::true_type{}, n, p0.s, p0.dp);
-      else finish(std::false_type{}, n, p0.s, p0.dp);
-    }
-  }
-};
-
 // ------------------------------------------------------------ key workgroups
 // One LDS buffer: row-major Q and dO blocks, their transposes (bf16), and the
 // block's L * log2(e) and D.
 template <typename T, int HD, int NW>
 struct KeyBuf {
-  using G = BwdGeo<T, HD, NW>;
+  using G = BlockGeo<T, HD, NW>;
   static constexpr size_t BYTES = (2 * G::NE + 2 * G::TE) * sizeof(T) + 2 * G::NB * sizeof(float);
   T* q; T* dO; T* qt; T* dOt; float* L; float* D;
   __device__ KeyBuf(char* base) {
@@ -346,7 +80,7 @@ struct KeyBuf {
 
 template <typename T, int HD, int NW>
 __device__ __forceinline__ void key_role(const BwdParams<T>& p, int bh, int kt, char* smem) {
-  using G = BwdGeo<T, HD, NW>;
+  using G = BlockGeo<T, HD, NW>;
   using M = typename G::M;
   using KB = KeyBuf<T, HD, NW>;
   constexpr bool BF = G::BF;
@@ -354,7 +88,6 @@ __device__ __forceinline__ void key_role(const BwdParams<T>& p, int bh, int kt, 
   constexpr uint32_t ROWB = G::ROWB;
   constexpr int BKV = NW * 32;
   static_assert(NB == 32, "L/D staging: lanes 0..31 hold L, lanes 32..63 hold D");
-  static_assert((BKV / NB) % 2 == 0, "the diagonal run must have an even length");
 
   const int S = p.S;
   const int tid = threadIdx.x, l = lane(), h = l >> 5, w = tid >> 6;
@@ -407,7 +140,7 @@ __device__ __forceinline__ void key_role(const BwdParams<T>& p, int bh, int kt, 
   // staged blocks in flight (set P holds the block written in iterations of
   // parity P); L and D are loaded by every thread (row tid % 32) so that all
   // waves count the same loads
-  using St = Stage2<T, HD, NW, true, true>;
+  using St = Stage2<T, HD, NW, true, true, true, true>;
   struct Staged {
     St x;
     float l = 0.f, d = 0.f;
@@ -604,8 +337,8 @@ __device__ __forceinline__ void key_role(const BwdParams<T>& p, int bh, int kt, 
       __syncthreads();
     }
   };
-  // causal: the first BKV/NB blocks cross the diagonal (an even count), or
-  // all of them if fewer remain; non-causal: none
+  // causal: the first BKV/NB blocks cross the diagonal (or all of them if
+  // fewer remain); non-causal: none
   int n = n0, par = 0;
   pipe.run(body, std::true_type{}, n, min(nm, nl), par);
   pipe.run(body, std::false_type{}, n, nl, par);
@@ -636,7 +369,7 @@ __device__ __forceinline__ void key_role(const BwdParams<T>& p, int bh, int kt, 
 // One LDS buffer: row-major K and V blocks and the transpose of K (bf16).
 template <typename T, int HD, int NW>
 struct QueryBuf {
-  using G = BwdGeo<T, HD, NW>;
+  using G = BlockGeo<T, HD, NW>;
   static constexpr size_t BYTES = (2 * G::NE + G::TE) * sizeof(T);
   T* k; T* v; T* kt;
   __device__ QueryBuf(char* base) {
@@ -648,14 +381,13 @@ struct QueryBuf {
 
 template <typename T, int HD, int NW>
 __device__ __forceinline__ void query_role(const BwdParams<T>& p, int bh, int qq, char* smem) {
-  using G = BwdGeo<T, HD, NW>;
+  using G = BlockGeo<T, HD, NW>;
   using M = typename G::M;
   using QB = QueryBuf<T, HD, NW>;
   constexpr bool BF = G::BF;
   constexpr int NB = G::NB, NDB = G::NDB, NC = G::NC, NU = G::NU, LD = G::LD;
   constexpr uint32_t ROWB = G::ROWB;
   constexpr int BQ = NW * 32;
-  static_assert((BQ / NB) % 2 == 0, "the unmasked run must have an even length");
 
   const int S = p.S;
   const int l = lane(), h = l >> 5, w = threadIdx.x >> 6;
@@ -705,7 +437,7 @@ __device__ __forceinline__ void query_role(const BwdParams<T>& p, int bh, int qq
   for (int d = 0; d < NDB; ++d) dqacc[d] = zero16();
 
   // staged blocks in flight (set P holds the block written in iterations of parity P)
-  using St = Stage2<T, HD, NW, true, false>;
+  using St = Stage2<T, HD, NW, true, true, true, false>;
   St a[2];
   constexpr int NLOAD = St::NLOAD;
   const u32x4s dKd = make_desc(p.K + hoff, head_bytes), dVd = make_desc(p.V + hoff, head_bytes);
@@ -788,8 +520,8 @@ __device__ __forceinline__ void query_role(const BwdParams<T>& p, int bh, int qq
     load(a[P], n + 4);         // last: volatile loads order the memory accesses around them
     __syncthreads();
   };
-  // causal: blocks [0, nm) are unmasked, nm = q0 / NB being a multiple of
-  // BQ / NB (even); non-causal: all are unmasked and there is no second run
+  // causal: blocks [0, nm) are unmasked and the rest cross the diagonal;
+  // non-causal: all are unmasked
   int n = 0, par = 0;
   Pipe::run(body, std::false_type{}, n, min(nm, nl), par);
   Pipe::run(body, std::true_type{}, n, nl, par);
