@@ -108,3 +108,11 @@ def test_empty_problem_is_a_no_op(call):
     assert call(S=0, **args) == OK
     assert call(B=0, **args) == OK
     assert call(H=0, **args) == OK
+
+
+def test_op_rejects_host_tensors():
+    # no CPU fallback: the op refuses tensors that are not on the GPU
+    torch = pytest.importorskip("torch")
+    q = torch.zeros(1, 1, 8, 16)
+    with pytest.raises(ValueError, match="GPU"):
+        xfa.flash_attention(q, q, q)

@@ -21,3 +21,5 @@ from ._binding import (  # noqa: F401
     xfa_fwd,
     xfa_status_string,
 )
+
+from .autograd import FlashAttentionFn, flash_attention  # noqa: E402,F401
