@@ -122,6 +122,7 @@ def cpu_baseline(x, n_heads: int):
     from oracle import attention_backward_head, attention_forward_head
 
     w = x.w
+    n_heads = max(1, min(n_heads, w.BH))
     cores = None
     try:
         from threadpoolctl import threadpool_info
