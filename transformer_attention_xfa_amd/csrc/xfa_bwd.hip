@@ -262,26 +262,37 @@ __device__ __forceinline__ void key_role(const BwdParams<T>& p, int bh, int kt, 
       typename M::frag qa[NC], oa[NC];
       const T* qrow = bn.q + (l & 31) * LD + M::KW * h;
       const T* orow = bn.dO + (l & 31) * LD + M::KW * h;
-  #pragma unroll
+#pragma unroll
       for (int c = 0; c < NC; ++c) {
         qa[c] = ld_nat(qrow + c * M::KD);
         oa[c] = ld_nat(orow + c * M::KD);
       }
       f32x4 L4[4], D4[4];
-  #pragma unroll
+#pragma unroll
       for (int g = 0; g < 4; ++g) {
         L4[g] = *reinterpret_cast<const f32x4*>(bc.L + 8 * g + 4 * h);
         D4[g] = *reinterpret_cast<const f32x4*>(bc.D + 8 * g + 4 * h);
       }
       const int lo = kj - (n * NB + 4 * h);      // masked: query row rel sees key kj iff rel >= lo
+      constexpr int NG = NU * NDB;               // gradient contraction pairs
+      // operands of the gradient contractions (transposed dO and Q of block
+      // n), read during the score steps into the registers the score
+      // operands free, so they are in flight before they are needed
+      typename M::frag ta[NG], tb[NG];
       sn = zero16();
       dn = zero16();
-  #pragma unroll
+#pragma unroll
       for (int c = 0; c < NC; ++c) {
         __builtin_amdgcn_sched_barrier(0);
         sn = M::mma(qa[c], kf[c], sn);
         dn = M::mma(oa[c], vf[c], dn);
-  #pragma unroll
+#pragma unroll
+        for (int g = c * NG / NC; g < (c + 1) * NG / NC; ++g) {
+          const int u = g / NDB, col = (g % NDB) * 32 + (l & 31);
+          ta[g] = *reinterpret_cast<const bf16x8*>(bc.dOt + 2 * TB::chunk_dw(col, 2 * u + h));
+          tb[g] = *reinterpret_cast<const bf16x8*>(bc.qt + 2 * TB::chunk_dw(col, 2 * u + h));
+        }
+#pragma unroll
         for (int v = c * EPC; v < (c + 1) * EPC && v < 16; ++v) {
           const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[v], p.c_log2, -L4[v >> 2][v & 3]));
           float ps = pr, ds = pr * (dp[v] - D4[v >> 2][v & 3]);
@@ -295,25 +306,18 @@ __device__ __forceinline__ void key_role(const BwdParams<T>& p, int bh, int kt, 
         }
       }
       __builtin_amdgcn_sched_barrier(0);
-      typename M::frag pf[NU], sf[NU], ta[NU][NDB], tb[NU][NDB];
-  #pragma unroll
+      typename M::frag pf[NU], sf[NU];
+#pragma unroll
       for (int u = 0; u < NU; ++u) {
         pf[u] = frag_from_acc(s, u, T{});
         sf[u] = frag_from_acc(dp, u, T{});
-  #pragma unroll
-        for (int d = 0; d < NDB; ++d) {
-          const int c = d * 32 + (l & 31);
-          ta[u][d] = *reinterpret_cast<const bf16x8*>(bc.dOt + 2 * TB::chunk_dw(c, 2 * u + h));
-          tb[u][d] = *reinterpret_cast<const bf16x8*>(bc.qt + 2 * TB::chunk_dw(c, 2 * u + h));
-        }
       }
-      constexpr int NG = NU * NDB;               // gradient contraction pairs
-  #pragma unroll
+#pragma unroll
       for (int g = 0; g < NG; ++g) {
         __builtin_amdgcn_sched_barrier(0);
         const int u = g / NDB, d = g % NDB;
-        dvacc[d] = M::mma(ta[u][d], pf[u], dvacc[d]);
-        dkacc[d] = M::mma(tb[u][d], sf[u], dkacc[d]);
+        dvacc[d] = M::mma(ta[g], pf[u], dvacc[d]);
+        dkacc[d] = M::mma(tb[g], sf[u], dkacc[d]);
         // the four store parts spread over the NG steps
 #pragma unroll
         for (int k = g * 4 / NG; k < (g + 1) * 4 / NG; ++k) a[P].x.store_part(k, bs.q, bs.dO, bs.qt, bs.dOt);
