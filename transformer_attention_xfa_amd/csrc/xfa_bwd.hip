@@ -66,14 +66,12 @@ struct BwdParams {
 template <typename T, int HD, int NW>
 struct KeyBuf {
   using G = BlockGeo<T, HD, NW>;
-  static constexpr size_t BYTES = (2 * G::NE + 2 * G::TE) * sizeof(T) + 2 * G::NB * sizeof(float);
-  T* q; T* dO; T* qt; T* dOt; float* L; float* D;
+  static constexpr size_t BYTES = 2 * G::NE * sizeof(T) + 2 * G::NB * sizeof(float);
+  T* q; T* dO; float* L; float* D;
   __device__ KeyBuf(char* base) {
     q = reinterpret_cast<T*>(base);
     dO = q + G::NE;
-    qt = dO + G::NE;
-    dOt = qt + G::TE;
-    L = reinterpret_cast<float*>(dOt + G::TE);
+    L = reinterpret_cast<float*>(dO + G::NE);
     D = L + G::NB;
   }
 };
@@ -112,8 +110,8 @@ __device__ __forceinline__ void key_role(const BwdParams<T>& p, int bh, int kt, 
 #pragma unroll
   for (int b = 0; b < 3; ++b) {
     KB kb(smem + b * KB::BYTES);
-    zero_pad<T, HD, NW>(kb.q, kb.qt);
-    zero_pad<T, HD, NW>(kb.dO, kb.dOt);
+    zero_pad<T, HD, NW>(kb.q, nullptr);
+    zero_pad<T, HD, NW>(kb.dO, nullptr);
   }
 
   // this lane's key row of K and V: B operands of S = Q.K^T and dP = dO.V^T
@@ -140,7 +138,7 @@ __device__ __forceinline__ void key_role(const BwdParams<T>& p, int bh, int kt, 
   // staged blocks in flight (set P holds the block written in iterations of
   // parity P); L and D are loaded by every thread (row tid % 32) so that all
   // waves count the same loads
-  using St = Stage2<T, HD, NW, true, true, true, true>;
+  using St = Stage2<T, HD, NW, true, true, false, false>;
   struct Staged {
     St x;
     float l = 0.f, d = 0.f;
@@ -204,14 +202,8 @@ __device__ __forceinline__ void key_role(const BwdParams<T>& p, int bh, int kt, 
 #pragma unroll
       for (int d = 0; d < NDB; ++d) {
         typename M::frag af, bf;
-        if constexpr (BF) {
-          const int c = d * 32 + (l & 31);
-          af = *reinterpret_cast<const bf16x8*>(b.dOt + 2 * TB::chunk_dw(c, 2 * u + h));
-          bf = *reinterpret_cast<const bf16x8*>(b.qt + 2 * TB::chunk_dw(c, 2 * u + h));
-        } else {
-          af = ld_res(b.dO, LD, 0, u, d * 32);
-          bf = ld_res(b.q, LD, 0, u, d * 32);
-        }
+        af = ld_res(b.dO, LD, 0, u, d * 32);
+        bf = ld_res(b.q, LD, 0, u, d * 32);
         dvacc[d] = M::mma(af, pf, dvacc[d]);
         dkacc[d] = M::mma(bf, sf, dkacc[d]);
       }
@@ -220,7 +212,7 @@ __device__ __forceinline__ void key_role(const BwdParams<T>& p, int bh, int kt, 
 
   auto put = [&](const Staged& z, int n) {
     KB b = buf(n);
-    z.x.store(b.q, b.dO, b.qt, b.dOt);
+    z.x.store(b.q, b.dO, nullptr, nullptr);
     // lanes 0..31 write L (log2 units) and lanes 32..63 write D of row
     // lane % 32; every wave writes the same values, which keeps the store
     // free of branches (a branch would split the scheduling region)
@@ -288,9 +280,9 @@ __device__ __forceinline__ void key_role(const BwdParams<T>& p, int bh, int kt, 
         dn = M::mma(oa[c], vf[c], dn);
 #pragma unroll
         for (int g = c * NG / NC; g < (c + 1) * NG / NC; ++g) {
-          const int u = g / NDB, col = (g % NDB) * 32 + (l & 31);
-          ta[g] = *reinterpret_cast<const bf16x8*>(bc.dOt + 2 * TB::chunk_dw(col, 2 * u + h));
-          tb[g] = *reinterpret_cast<const bf16x8*>(bc.qt + 2 * TB::chunk_dw(col, 2 * u + h));
+          const int u = g / NDB;
+          ta[g] = ld_res(bc.dO, LD, 0, u, (g % NDB) * 32);
+          tb[g] = ld_res(bc.q, LD, 0, u, (g % NDB) * 32);
         }
 #pragma unroll
         for (int v = c * EPC; v < (c + 1) * EPC && v < 16; ++v) {
@@ -320,7 +312,7 @@ __device__ __forceinline__ void key_role(const BwdParams<T>& p, int bh, int kt, 
         dkacc[d] = M::mma(tb[g], sf[u], dkacc[d]);
         // the four store parts spread over the NG steps
 #pragma unroll
-        for (int k = g * 4 / NG; k < (g + 1) * 4 / NG; ++k) a[P].x.store_part(k, bs.q, bs.dO, bs.qt, bs.dOt);
+        for (int k = g * 4 / NG; k < (g + 1) * 4 / NG; ++k) a[P].x.store_part(k, bs.q, bs.dO, nullptr, nullptr);
         if (g == 0) bs.L[l] = (l < NB) ? a[P].l * kLog2e : a[P].d;
       }
       __builtin_amdgcn_sched_barrier(0);

@@ -231,7 +231,8 @@ __device__ inline void zero_pad(T* nat, T* tr) {
       nat[r * G::LD + c] = (T)0.f;
     }
     if constexpr (G::BF)
-      for (int e = threadIdx.x; e < (G::HDP - HD) * G::NB; e += G::NT) tr[HD * G::NB + e] = (T)0.f;
+      if (tr != nullptr)
+        for (int e = threadIdx.x; e < (G::HDP - HD) * G::NB; e += G::NT) tr[HD * G::NB + e] = (T)0.f;
   }
 }
 
