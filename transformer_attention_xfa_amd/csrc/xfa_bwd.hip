@@ -35,15 +35,14 @@
 // evaluate them.  A query workgroup runs two waves per SIMD instead and
 // finishes each block in its own iteration.
 //
-// For bf16 the operands whose contraction index runs along block rows (dO^T,
-// Q^T for the key workgroups, K^T for the query workgroups) are also written
-// into LDS transposed (TTile), so every operand fragment is one 16-byte read.
-// A block is staged in units of 4 rows x one 16-byte column chunk: the four
-// 16-byte loads of a unit give both its row-major copy and, by byte permutes,
-// its transposed copy.  Rows past the sequence end load as zeros, and with
-// zero Q / dO (or K / V) rows such pairs add nothing, so only blocks at the
-// causal diagonal evaluate the mask.  The factor `scale` of ds is applied
-// once, to dK and dQ when they are written.
+// The operands whose contraction index runs along block rows (dO^T and Q^T
+// for the key workgroups, K^T for the query workgroups) are read from the
+// row-major tiles with the LDS transpose read (ds_read_b64_tr_b16 for bf16),
+// so every block is staged once, row-major.  A block is staged in units of 4
+// rows x one 16-byte column chunk.  Rows past the sequence end load as zeros,
+// and with zero Q / dO (or K / V) rows such pairs add nothing, so only blocks
+// at the causal diagonal evaluate the mask.  The factor `scale` of ds is
+// applied once, to dK and dQ when they are written.
 #include <type_traits>
 
 #include "xfa_common.h"
@@ -366,12 +365,11 @@ __device__ __forceinline__ void key_role(const BwdParams<T>& p, int bh, int kt, 
 template <typename T, int HD, int NW>
 struct QueryBuf {
   using G = BlockGeo<T, HD, NW>;
-  static constexpr size_t BYTES = (2 * G::NE + G::TE) * sizeof(T);
-  T* k; T* v; T* kt;
+  static constexpr size_t BYTES = 2 * G::NE * sizeof(T);
+  T* k; T* v;
   __device__ QueryBuf(char* base) {
     k = reinterpret_cast<T*>(base);
     v = k + G::NE;
-    kt = v + G::NE;
   }
 };
 
@@ -408,8 +406,8 @@ __device__ __forceinline__ void query_role(const BwdParams<T>& p, int bh, int qq
 #pragma unroll
   for (int b = 0; b < 3; ++b) {
     QB qb(smem + b * QB::BYTES);
-    zero_pad<T, HD, NW>(qb.k, qb.kt);
-    zero_pad<T, HD, NW>(qb.v, qb.kt);
+    zero_pad<T, HD, NW>(qb.k, nullptr);
+    zero_pad<T, HD, NW>(qb.v, nullptr);
   }
 
   // this lane's query row of Q and dO: B operands of S^T = K.Q^T and dP^T = V.dO^T
@@ -433,14 +431,14 @@ __device__ __forceinline__ void query_role(const BwdParams<T>& p, int bh, int qq
   for (int d = 0; d < NDB; ++d) dqacc[d] = zero16();
 
   // staged blocks in flight (set P holds the block written in iterations of parity P)
-  using St = Stage2<T, HD, NW, true, true, true, false>;
+  using St = Stage2<T, HD, NW, true, true, false, false>;
   St a[2];
   constexpr int NLOAD = St::NLOAD;
   const u32x4s dKd = make_desc(p.K + hoff, head_bytes), dVd = make_desc(p.V + hoff, head_bytes);
   auto load = [&](St& z, int n) { z.load(dKd, dVd, n * NB); };
   auto put = [&](const St& z, int n) {
     QB b = buf(n);
-    z.store(b.k, b.v, b.kt, nullptr);
+    z.store(b.k, b.v, nullptr, nullptr);
   };
 
   // S^T and dP^T of block n: C tiles with column = this lane's query, rows = keys
@@ -477,10 +475,7 @@ __device__ __forceinline__ void query_role(const BwdParams<T>& p, int bh, int qq
 #pragma unroll
       for (int d = 0; d < NDB; ++d) {
         typename M::frag af;
-        if constexpr (BF)
-          af = *reinterpret_cast<const bf16x8*>(b.kt + 2 * TB::chunk_dw(d * 32 + (l & 31), 2 * u + h));
-        else
-          af = ld_res(b.k, LD, 0, u, d * 32);
+        af = ld_res(b.k, LD, 0, u, d * 32);
         dqacc[d] = M::mma(af, sf, dqacc[d]);
       }
     }
