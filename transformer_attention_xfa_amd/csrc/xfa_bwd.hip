@@ -60,18 +60,18 @@ struct BwdParams {
 };
 
 // ------------------------------------------------------------ key workgroups
-// One LDS buffer: row-major Q and dO blocks, their transposes (bf16), and the
-// block's L * log2(e) and D.
+// One LDS buffer: row-major Q and dO blocks (row stride LD) and the block's
+// L and D, as the DMA image Dma<..., 2, true> lays them out.
 template <typename T, int HD, int NW>
 struct KeyBuf {
-  using G = BlockGeo<T, HD, NW>;
-  static constexpr size_t BYTES = 2 * G::NE * sizeof(T) + 2 * G::NB * sizeof(float);
+  using DM = Dma<T, HD, NW, 2, true>;
+  static constexpr size_t BYTES = DM::BYTES;
   T* q; T* dO; float* L; float* D;
   __device__ KeyBuf(char* base) {
     q = reinterpret_cast<T*>(base);
-    dO = q + G::NE;
-    L = reinterpret_cast<float*>(dO + G::NE);
-    D = L + G::NB;
+    dO = reinterpret_cast<T*>(base + DM::TILE);
+    L = reinterpret_cast<float*>(base + 2 * DM::TILE);
+    D = reinterpret_cast<float*>(base + 2 * DM::TILE + 1024);
   }
 };
 
@@ -84,18 +84,13 @@ __device__ __forceinline__ void key_role(const BwdParams<T>& p, int bh, int kt, 
   constexpr int NB = G::NB, NDB = G::NDB, NC = G::NC, NU = G::NU, LD = G::LD;
   constexpr uint32_t ROWB = G::ROWB;
   constexpr int BKV = NW * 32;
-  static_assert(NB == 32, "L/D staging: lanes 0..31 hold L, lanes 32..63 hold D");
 
   const int S = p.S;
   const int tid = threadIdx.x, l = lane(), h = l >> 5, w = tid >> 6;
   const size_t hoff = (size_t)bh * S * HD;
   const uint32_t head_bytes = (uint32_t)S * ROWB;
-  const rsrc_t rQ = make_rsrc(p.Q + hoff, head_bytes);
   const rsrc_t rK = make_rsrc(p.K + hoff, head_bytes);
   const rsrc_t rV = make_rsrc(p.V + hoff, head_bytes);
-  const rsrc_t rdO = make_rsrc(p.dO + hoff, head_bytes);
-  const rsrc_t rL = make_rsrc(p.Lse + (size_t)bh * S, (uint32_t)S * 4u);
-  const rsrc_t rD = make_rsrc(p.Dl + (size_t)bh * S, (uint32_t)S * 4u);
 
   const int j0 = kt * BKV;                       // first key of the workgroup
   const int kj = j0 + 32 * w + (l & 31);         // this lane's key
@@ -105,13 +100,7 @@ __device__ __forceinline__ void key_role(const BwdParams<T>& p, int bh, int kt, 
   const int nm = p.causal ? min(nb, n0 + BKV / NB) : n0;
   const int nl = nb - 1;
 
-  auto buf = [&](int n) { return KB(smem + (size_t)(n % 3) * KB::BYTES); };
-#pragma unroll
-  for (int b = 0; b < 3; ++b) {
-    KB kb(smem + b * KB::BYTES);
-    zero_pad<T, HD, NW>(kb.q, nullptr);
-    zero_pad<T, HD, NW>(kb.dO, nullptr);
-  }
+  auto buf = [&](int n) { return KB(smem + (size_t)(n & 3) * KB::BYTES); };
 
   // this lane's key row of K and V: B operands of S = Q.K^T and dP = dO.V^T
   typename M::frag kf[NC], vf[NC];
@@ -134,27 +123,15 @@ __device__ __forceinline__ void key_role(const BwdParams<T>& p, int bh, int kt, 
     dvacc[d] = zero16();
   }
 
-  // staged blocks in flight (set P holds the block written in iterations of
-  // parity P); L and D are loaded by every thread (row tid % 32) so that all
-  // waves count the same loads
-  using St = Stage2<T, HD, NW, true, true, false, false>;
-  struct Staged {
-    St x;
-    float l = 0.f, d = 0.f;
-  } a[2];
-  constexpr int NLOAD = St::NLOAD + 2;           // loads per staged block
-  const u32x4s dQd = make_desc(p.Q + hoff, head_bytes), ddOd = make_desc(p.dO + hoff, head_bytes);
-  const u32x4s dLd = make_desc(p.Lse + (size_t)bh * S, (uint32_t)S * 4u);
-  const u32x4s dDd = make_desc(p.Dl + (size_t)bh * S, (uint32_t)S * 4u);
-  auto load = [&](Staged& z, int n) {
-    z.x.load(dQd, ddOd, n * NB);
-    z.l = asm_load4(dLd, (uint32_t)(n * NB + (tid & (NB - 1))) * 4u);
-    z.d = asm_load4(dDd, (uint32_t)(n * NB + (tid & (NB - 1))) * 4u);
-  };
-  // wait until at most N loads are in flight, which lands set z
-  auto ready = [&](auto n_after, Staged& z) { wait_vm<decltype(n_after)::value>(z.x.x, z.l, z.d); };
-  using Zero = std::integral_constant<int, 0>;
-  using One = std::integral_constant<int, NLOAD>;
+  // Blocks rotate through four LDS buffers filled by DMA: block m is fetched
+  // two iterations before it is first read (see the loop body).
+  using DM = typename KB::DM;
+  constexpr int NPW = DM::NPW;
+  DM dma;
+  dma.init({make_desc(p.Q + hoff, head_bytes), make_desc(p.dO + hoff, head_bytes)},
+           make_desc(p.Lse + (size_t)bh * S, (uint32_t)S * 4u), make_desc(p.Dl + (size_t)bh * S, (uint32_t)S * 4u));
+  const uint32_t smem0 = lds_addr(smem);
+  auto fetch = [&](int n) { dma.issue(smem0 + (uint32_t)(n & 3) * KB::BYTES, n * NB); };
   // S and dP of block n: C tiles with column = this lane's key, rows = queries
   auto sdp = [&](int n, f32x16& s, f32x16& dp) {
     KB b = buf(n);
@@ -179,7 +156,7 @@ __device__ __forceinline__ void key_role(const BwdParams<T>& p, int bh, int kt, 
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int v = 4 * g + e;
-        const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[v], p.c_log2, -L4[e]));
+        const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[v], p.c_log2, -L4[e] * kLog2e));
         s[v] = pr;
         dp[v] = pr * (dp[v] - D4[e]);
       }
@@ -209,15 +186,6 @@ __device__ __forceinline__ void key_role(const BwdParams<T>& p, int bh, int kt, 
     }
   };
 
-  auto put = [&](const Staged& z, int n) {
-    KB b = buf(n);
-    z.x.store(b.q, b.dO, nullptr, nullptr);
-    // lanes 0..31 write L (log2 units) and lanes 32..63 write D of row
-    // lane % 32; every wave writes the same values, which keeps the store
-    // free of branches (a branch would split the scheduling region)
-    b.L[l] = (l < NB) ? z.l * kLog2e : z.d;
-  };
-
   // the compiler's own loads (kf, vf) land before the staging loads start
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
@@ -225,28 +193,22 @@ __device__ __forceinline__ void key_role(const BwdParams<T>& p, int bh, int kt, 
     settle(vf[c]);
   }
   f32x16 sa, pa, sb, pb;
-  load(a[0], n0);
-  ready(Zero{}, a[0]);
-  put(a[0], n0);
-  load(a[0], n0 + 1);
-  ready(Zero{}, a[0]);
-  put(a[0], n0 + 1);
-  load(a[0], n0 + 2);
-  load(a[1], n0 + 3);
+  fetch(n0);
+  fetch(n0 + 1);
+  fetch(n0 + 2);
+  wait_vm<NPW>();              // blocks n0, n0+1 landed; n0+2 in flight
   __syncthreads();
   sdp(n0, sa, pa);
   Pipe pipe(sa, pa, sb, pb);
   // bf16 iteration with the work interleaved by hand (sched_barrier fences
   // keep the order): the score contractions of block n+1 alternate with the
-  // exponentials and dS of block n, and the gradient contractions of block n
-  // with the staging writes of block n+2.  Same arithmetic as sdp() then
-  // finish().
+  // exponentials and dS of block n and the reads of block n's gradient
+  // operands.  Same arithmetic as sdp() then finish().
   auto fused = [&](auto masked, auto par, int n) {
     if constexpr (BF) {
-      constexpr int P = decltype(par)::value;
       constexpr int EPC = (16 + NC - 1) / NC;    // score elements finished per contraction step
-      ready(One{}, a[P]);        // set P landed; set 1-P (one block behind) in flight
-      KB bn = buf(n + 1), bc = buf(n), bs = buf(n + 2);
+      fetch(n + 3);              // into the buffer of block n-1, finished before the last barrier
+      KB bn = buf(n + 1), bc = buf(n);
       f32x16& sn = pipe.next(par).s;
       f32x16& dn = pipe.next(par).dp;
       f32x16 s = pipe.cur(par).s, dp = pipe.cur(par).dp;
@@ -285,7 +247,7 @@ __device__ __forceinline__ void key_role(const BwdParams<T>& p, int bh, int kt, 
         }
 #pragma unroll
         for (int v = c * EPC; v < (c + 1) * EPC && v < 16; ++v) {
-          const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[v], p.c_log2, -L4[v >> 2][v & 3]));
+          const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[v], p.c_log2, -L4[v >> 2][v & 3] * kLog2e));
           float ps = pr, ds = pr * (dp[v] - D4[v >> 2][v & 3]);
           if constexpr (decltype(masked)::value) {
             const bool keep = 8 * (v >> 2) + (v & 3) >= lo;
@@ -309,13 +271,9 @@ __device__ __forceinline__ void key_role(const BwdParams<T>& p, int bh, int kt, 
         const int u = g / NDB, d = g % NDB;
         dvacc[d] = M::mma(ta[g], pf[u], dvacc[d]);
         dkacc[d] = M::mma(tb[g], sf[u], dkacc[d]);
-        // the four store parts spread over the NG steps
-#pragma unroll
-        for (int k = g * 4 / NG; k < (g + 1) * 4 / NG; ++k) a[P].x.store_part(k, bs.q, bs.dO, nullptr, nullptr);
-        if (g == 0) bs.L[l] = (l < NB) ? a[P].l * kLog2e : a[P].d;
       }
       __builtin_amdgcn_sched_barrier(0);
-      load(a[P], n + 4);         // last: volatile loads order the memory accesses around them
+      wait_vm<NPW>();            // block n+2 landed; n+3 in flight
       __syncthreads();
     }
   };
@@ -323,12 +281,10 @@ __device__ __forceinline__ void key_role(const BwdParams<T>& p, int bh, int kt, 
     if constexpr (BF) {
       fused(masked, par, n);
     } else {
-      constexpr int P = decltype(par)::value;
-      ready(One{}, a[P]);      // set P landed; set 1-P (one block behind) in flight
+      fetch(n + 3);            // into the buffer of block n-1, finished before the last barrier
       sdp(n + 1, pipe.next(par).s, pipe.next(par).dp);
-      put(a[P], n + 2);
       finish(masked, n, pipe.cur(par).s, pipe.cur(par).dp);
-      load(a[P], n + 4);       // last: volatile loads order the memory accesses around them
+      wait_vm<NPW>();          // block n+2 landed; n+3 in flight
       __syncthreads();
     }
   };
@@ -338,10 +294,7 @@ __device__ __forceinline__ void key_role(const BwdParams<T>& p, int bh, int kt, 
   pipe.run(body, std::true_type{}, n, min(nm, nl), par);
   pipe.run(body, std::false_type{}, n, nl, par);
   pipe.last(finish, nl < nm, nl, par);
-  // drain the loads of blocks past the end; their registers stay reserved
-  // until the loads have landed
-  ready(Zero{}, a[0]);
-  ready(Zero{}, a[1]);
+  wait_vm<0>();                // the fetches of blocks past the end write LDS: drain them
 
   // dK_j (scaled), dV_j for this lane's key: C tile column = key, rows = d
   const rsrc_t rdK = make_rsrc(p.dK + hoff, head_bytes);
@@ -361,15 +314,16 @@ __device__ __forceinline__ void key_role(const BwdParams<T>& p, int bh, int kt, 
 }
 
 // ---------------------------------------------------------- query workgroups
-// One LDS buffer: row-major K and V blocks and the transpose of K (bf16).
+// One LDS buffer: row-major K and V blocks (row stride LD), as the DMA image
+// Dma<..., 2, false> lays them out.
 template <typename T, int HD, int NW>
 struct QueryBuf {
-  using G = BlockGeo<T, HD, NW>;
-  static constexpr size_t BYTES = 2 * G::NE * sizeof(T);
+  using DM = Dma<T, HD, NW, 2, false>;
+  static constexpr size_t BYTES = DM::BYTES;
   T* k; T* v;
   __device__ QueryBuf(char* base) {
     k = reinterpret_cast<T*>(base);
-    v = k + G::NE;
+    v = reinterpret_cast<T*>(base + DM::TILE);
   }
 };
 
@@ -388,8 +342,6 @@ __device__ __forceinline__ void query_role(const BwdParams<T>& p, int bh, int qq
   const size_t hoff = (size_t)bh * S * HD;
   const uint32_t head_bytes = (uint32_t)S * ROWB;
   const rsrc_t rQ = make_rsrc(p.Q + hoff, head_bytes);
-  const rsrc_t rK = make_rsrc(p.K + hoff, head_bytes);
-  const rsrc_t rV = make_rsrc(p.V + hoff, head_bytes);
   const rsrc_t rdO = make_rsrc(p.dO + hoff, head_bytes);
   const rsrc_t rL = make_rsrc(p.Lse + (size_t)bh * S, (uint32_t)S * 4u);
   const rsrc_t rD = make_rsrc(p.Dl + (size_t)bh * S, (uint32_t)S * 4u);
@@ -402,13 +354,7 @@ __device__ __forceinline__ void query_role(const BwdParams<T>& p, int bh, int qq
   const int nm = p.causal ? q0 / NB : nb;
   const int nl = nb - 1;
 
-  auto buf = [&](int n) { return QB(smem + (size_t)(n % 3) * QB::BYTES); };
-#pragma unroll
-  for (int b = 0; b < 3; ++b) {
-    QB qb(smem + b * QB::BYTES);
-    zero_pad<T, HD, NW>(qb.k, nullptr);
-    zero_pad<T, HD, NW>(qb.v, nullptr);
-  }
+  auto buf = [&](int n) { return QB(smem + (size_t)(n & 3) * QB::BYTES); };
 
   // this lane's query row of Q and dO: B operands of S^T = K.Q^T and dP^T = V.dO^T
   typename M::frag qf[NC], of[NC];
@@ -430,16 +376,15 @@ __device__ __forceinline__ void query_role(const BwdParams<T>& p, int bh, int qq
 #pragma unroll
   for (int d = 0; d < NDB; ++d) dqacc[d] = zero16();
 
-  // staged blocks in flight (set P holds the block written in iterations of parity P)
-  using St = Stage2<T, HD, NW, true, true, false, false>;
-  St a[2];
-  constexpr int NLOAD = St::NLOAD;
-  const u32x4s dKd = make_desc(p.K + hoff, head_bytes), dVd = make_desc(p.V + hoff, head_bytes);
-  auto load = [&](St& z, int n) { z.load(dKd, dVd, n * NB); };
-  auto put = [&](const St& z, int n) {
-    QB b = buf(n);
-    z.store(b.k, b.v, nullptr, nullptr);
-  };
+  // Blocks rotate through four LDS buffers filled by DMA: block m is fetched
+  // two iterations before it is read.
+  using DM = typename QB::DM;
+  constexpr int NPW = DM::NPW;
+  DM dma;
+  const u32x4s dK = make_desc(p.K + hoff, head_bytes);
+  dma.init({dK, make_desc(p.V + hoff, head_bytes)}, dK, dK);
+  const uint32_t smem0 = lds_addr(smem);
+  auto fetch = [&](int n) { dma.issue(smem0 + (uint32_t)(n & 3) * QB::BYTES, n * NB); };
 
   // S^T and dP^T of block n: C tiles with column = this lane's query, rows = keys
   auto sdp = [&](int n, f32x16& s, f32x16& dp) {
@@ -481,7 +426,7 @@ __device__ __forceinline__ void query_role(const BwdParams<T>& p, int bh, int qq
     }
   };
 
-  // the compiler's own loads (qf, of, L, D) land before the staging loads start
+  // the compiler's own loads (qf, of, L, D) land before the DMA starts
   settle(L2);
   settle(Di);
 #pragma unroll
@@ -492,23 +437,17 @@ __device__ __forceinline__ void query_role(const BwdParams<T>& p, int bh, int qq
   // One block per iteration, score and gradient contractions back to back:
   // this kernel runs two waves per SIMD (it fits in half the register
   // file), and the other wave's work overlaps each wave's waits.
-  load(a[0], 0);
-  wait_vm<0>(a[0].x);
-  put(a[0], 0);
-  load(a[0], 1);
-  wait_vm<0>(a[0].x);
-  put(a[0], 1);
-  load(a[0], 2);
-  load(a[1], 3);
+  fetch(0);
+  fetch(1);
+  fetch(2);
+  wait_vm<2 * NPW>();          // block 0 landed; 1 and 2 in flight
   __syncthreads();
-  auto body = [&](auto masked, auto par, int n) {
-    constexpr int P = decltype(par)::value;
+  auto body = [&](auto masked, auto, int n) {
+    fetch(n + 3);              // into the buffer of block n-1, finished before the last barrier
     f32x16 s, dp;
     sdp(n, s, dp);
-    wait_vm<NLOAD>(a[P].x);    // set P landed; set 1-P (one block behind) in flight
-    put(a[P], n + 2);
     finish(masked, n, s, dp);
-    load(a[P], n + 4);         // last: volatile loads order the memory accesses around them
+    wait_vm<2 * NPW>();        // block n+1 landed; n+2 and n+3 in flight
     __syncthreads();
   };
   // causal: blocks [0, nm) are unmasked and the rest cross the diagonal;
@@ -522,10 +461,7 @@ __device__ __forceinline__ void query_role(const BwdParams<T>& p, int bh, int qq
     if (nl >= nm) finish(std::true_type{}, nl, s, dp);
     else finish(std::false_type{}, nl, s, dp);
   }
-  // drain the loads of blocks past the end; their registers stay reserved
-  // until the loads have landed
-  wait_vm<0>(a[0].x);
-  wait_vm<0>(a[1].x);
+  wait_vm<0>();                // the fetches of blocks past the end write LDS: drain them
 
   // dQ_i (scaled): C tile column = query, rows = d
   const rsrc_t rdQ = make_rsrc(p.dQ + hoff, head_bytes);
@@ -544,8 +480,8 @@ __device__ __forceinline__ void query_role(const BwdParams<T>& p, int bh, int qq
 template <typename T, int HD>
 struct BwdCfg {
   static constexpr int NW = 4;
-  static constexpr size_t KEY_BYTES = 3 * KeyBuf<T, HD, NW>::BYTES;
-  static constexpr size_t QUERY_BYTES = 3 * QueryBuf<T, HD, NW>::BYTES;
+  static constexpr size_t KEY_BYTES = 4 * KeyBuf<T, HD, NW>::BYTES;     // four rotating buffers
+  static constexpr size_t QUERY_BYTES = 4 * QueryBuf<T, HD, NW>::BYTES;
   static constexpr size_t SMEM = KEY_BYTES > QUERY_BYTES ? KEY_BYTES : QUERY_BYTES;
 };
 

@@ -286,3 +286,87 @@ struct Pipe {
 };
 
 }  // namespace xfa
+
+namespace xfa {
+
+// ------------------------------------------------ blocks copied by DMA
+// The LDS image of a 32-row block of a [S][HD] tensor (row stride LD
+// elements) is filled by buffer loads that write LDS directly
+// (`buffer_load_dwordx4 ... lds`): each such load moves 64 x 16 bytes from
+// per-lane global offsets to 1 KiB of consecutive LDS bytes starting at M0.
+// Slot s of the image (16 bytes at byte 16 s) holds chunk s % SPR of block
+// row s / SPR; the slots of the row padding and rows past the tensor read out
+// of range, which writes zeros, so padding and ragged tails come out zero.
+// No registers hold staged data.  Strips (1 KiB) of a block are dealt to the
+// waves round robin; every wave issues the same number of loads per block,
+// so a wave's wait count is a constant.
+__device__ inline void dma16(const u32x4s& d, uint32_t off, uint32_t lds_byte) {
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" :: "v"(off), "s"(d), "{m0}"(lds_byte) : "memory");
+}
+__device__ inline uint32_t lds_addr(const void* p) {
+  return (uint32_t)(size_t)((__attribute__((address_space(3))) const char*)p);
+}
+
+// NTEN tensors of [S][HD] rows plus, when ROWS_F32, two fp32 [S] vectors (L
+// and D): per block the image is NTEN tiles of NI strips, then one strip for
+// each vector (its first 128 bytes).  Each wave's strips are fixed, so their
+// descriptors, LDS offsets and source offsets are worked out once (init) and
+// a block costs NPW loads and a few scalar operations, with no branches.
+template <typename T, int HD, int NW, int NTEN, bool ROWS_F32>
+struct Dma {
+  using G = BlockGeo<T, HD, NW>;
+  static constexpr int SPR = G::LD * (int)sizeof(T) / 16;   // 16-byte slots per LDS row
+  static constexpr int NI = (G::NB * SPR + 63) / 64;        // strips per tensor tile
+  static constexpr int TILE = NI * 1024;                    // bytes of a tensor tile
+  static constexpr int NS = NTEN * NI + (ROWS_F32 ? 2 : 0); // strips per block
+  static constexpr int NPW = (NS + NW - 1) / NW;            // strips per wave per block
+  static constexpr int BYTES = NTEN * TILE + (ROWS_F32 ? 2048 : 0);
+  static_assert(G::LD * sizeof(T) % 16 == 0, "LDS rows must be whole slots");
+  u32x4s desc[NPW];    // source tensor of each of this wave's strips
+  uint32_t dst[NPW];   // its LDS byte offset in the image
+  uint32_t step[NPW];  // source bytes per block row (ROWB or 4)
+  uint32_t rel[NPW];   // this lane's source byte offset at block row 0
+
+  __device__ inline void init(const u32x4s (&dt)[NTEN], const u32x4s& dl, const u32x4s& dd) {
+    const int l = lane();
+    const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+#pragma unroll
+    for (int t = 0; t < NPW; ++t) {
+      int j = w + NW * t;
+      // a wave past the last strip loads one again: the same bytes to the
+      // same place, so the duplicate is harmless and every wave counts NPW
+      if (j >= NS) j -= NS;
+      uint32_t r = 0x80000000u;                // out of range: writes zeros
+      if (j < NTEN * NI) {
+        const int ten = j / NI, i = j % NI;
+        u32x4s d = dt[0];
+#pragma unroll
+        for (int e = 1; e < NTEN; ++e)
+          if (ten == e) d = dt[e];
+        desc[t] = d;
+        dst[t] = (uint32_t)ten * TILE + (uint32_t)i * 1024u;
+        step[t] = G::ROWB;
+        const int s = 64 * i + l, row = s / SPR, ch = s % SPR;
+        if (row < G::NB && ch < G::CPR) r = (uint32_t)row * G::ROWB + (uint32_t)ch * 16u;
+      } else {
+        desc[t] = (j == NTEN * NI) ? dl : dd;
+        dst[t] = (uint32_t)NTEN * TILE + (uint32_t)(j - NTEN * NI) * 1024u;
+        step[t] = 4u;
+        if (l < G::NB / 4) r = (uint32_t)l * 16u;   // 4 fp32 rows per lane
+      }
+      rel[t] = r;
+    }
+  }
+  // Issue this wave's strips of block rows [row0, row0 + NB) into the image
+  // at LDS byte `base`.
+  __device__ inline void issue(uint32_t base, int row0) const {
+#pragma unroll
+    for (int t = 0; t < NPW; ++t) {
+      // an out-of-range slot stays out of range whatever the row offset
+      const uint32_t off = (rel[t] + (uint32_t)row0 * step[t]) | (rel[t] & 0x80000000u);
+      dma16(desc[t], off, base + dst[t]);
+    }
+  }
+};
+
+}  // namespace xfa
