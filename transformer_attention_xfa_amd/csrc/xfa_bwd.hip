@@ -212,26 +212,38 @@ __device__ __forceinline__ void key_role(const BwdParams<T>& p, int bh, int kt, 
       f32x16& sn = pipe.next(par).s;
       f32x16& dn = pipe.next(par).dp;
       f32x16 s = pipe.cur(par).s, dp = pipe.cur(par).dp;
-      typename M::frag qa[NC], oa[NC];
       const T* qrow = bn.q + (l & 31) * LD + M::KW * h;
       const T* orow = bn.dO + (l & 31) * LD + M::KW * h;
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        qa[c] = ld_nat(qrow + c * M::KD);
-        oa[c] = ld_nat(orow + c * M::KD);
-      }
-      f32x4 L4[4], D4[4];
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        L4[g] = *reinterpret_cast<const f32x4*>(bc.L + 8 * g + 4 * h);
-        D4[g] = *reinterpret_cast<const f32x4*>(bc.D + 8 * g + 4 * h);
-      }
       const int lo = kj - (n * NB + 4 * h);      // masked: query row rel sees key kj iff rel >= lo
       constexpr int NG = NU * NDB;               // gradient contraction pairs
-      // operands of the gradient contractions (transposed dO and Q of block
-      // n), read during the score steps into the registers the score
-      // operands free, so they are in flight before they are needed
-      typename M::frag ta[NG], tb[NG];
+      // LDS reads are spread over the contraction steps so that the matrix
+      // core never waits behind a long queue of them: the score operands are
+      // read PD steps ahead, L and D of block n one row group ahead of the
+      // exponentials, and the transposed dO and Q operands of block n (the
+      // gradient contractions' A operands) NGA pairs during the score steps
+      // and the rest NGA pairs ahead during the gradient steps.
+      constexpr int PD = 2;
+      constexpr int NGA = NG / 2;
+      typename M::frag qa[NC], oa[NC], ta[NG], tb[NG];
+      f32x4 L4[4], D4[4];
+      auto read_ld = [&](int g) {
+        L4[g] = *reinterpret_cast<const f32x4*>(bc.L + 8 * g + 4 * h);
+        D4[g] = *reinterpret_cast<const f32x4*>(bc.D + 8 * g + 4 * h);
+      };
+      auto read_sc = [&](int c) {
+        qa[c] = ld_nat(qrow + c * M::KD);
+        oa[c] = ld_nat(orow + c * M::KD);
+      };
+      auto read_tr = [&](int g) {
+        ta[g] = ld_res(bc.dO, LD, 0, g / NDB, (g % NDB) * 32);
+        tb[g] = ld_res(bc.q, LD, 0, g / NDB, (g % NDB) * 32);
+      };
+      // row group g of L and D is first needed at step 4 g / EPC
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        if (4 * g / EPC == 0) read_ld(g);
+#pragma unroll
+      for (int c = 0; c < PD && c < NC; ++c) read_sc(c);
       sn = zero16();
       dn = zero16();
 #pragma unroll
@@ -239,12 +251,12 @@ __device__ __forceinline__ void key_role(const BwdParams<T>& p, int bh, int kt, 
         __builtin_amdgcn_sched_barrier(0);
         sn = M::mma(qa[c], kf[c], sn);
         dn = M::mma(oa[c], vf[c], dn);
+        if (c + PD < NC) read_sc(c + PD);
 #pragma unroll
-        for (int g = c * NG / NC; g < (c + 1) * NG / NC; ++g) {
-          const int u = g / NDB;
-          ta[g] = ld_res(bc.dO, LD, 0, u, (g % NDB) * 32);
-          tb[g] = ld_res(bc.q, LD, 0, u, (g % NDB) * 32);
-        }
+        for (int g = 1; g < 4; ++g)
+          if (4 * g / EPC == c + 1) read_ld(g);
+#pragma unroll
+        for (int g = c * NGA / NC; g < (c + 1) * NGA / NC; ++g) read_tr(g);
 #pragma unroll
         for (int v = c * EPC; v < (c + 1) * EPC && v < 16; ++v) {
           const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[v], p.c_log2, -L4[v >> 2][v & 3] * kLog2e));
@@ -271,6 +283,7 @@ __device__ __forceinline__ void key_role(const BwdParams<T>& p, int bh, int kt, 
         const int u = g / NDB, d = g % NDB;
         dvacc[d] = M::mma(ta[g], pf[u], dvacc[d]);
         dkacc[d] = M::mma(tb[g], sf[u], dkacc[d]);
+        if (g + NGA < NG) read_tr(g + NGA);
       }
       __builtin_amdgcn_sched_barrier(0);
       wait_vm<NPW>();            // block n+2 landed; n+3 in flight
