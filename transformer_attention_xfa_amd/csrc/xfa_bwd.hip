@@ -60,12 +60,13 @@ struct BwdParams {
 };
 
 // ------------------------------------------------------------ key workgroups
-// One LDS buffer: row-major Q and dO blocks (row stride LD) and the block's
-// L and D, as the DMA image Dma<..., 2, true> lays them out.
+// One LDS buffer: the images of the Q and dO blocks and the block's L and
+// D, as Dma<..., 2, true> lays them out.
 template <typename T, int HD, int NW>
 struct KeyBuf {
   using DM = Dma<T, HD, NW, 2, true>;
   static constexpr size_t BYTES = DM::BYTES;
+  static constexpr int NBUF = 4;   // rotating buffers (a fifth, fetched earlier, measured slower)
   T* q; T* dO; float* L; float* D;
   __device__ KeyBuf(char* base) {
     q = reinterpret_cast<T*>(base);
@@ -81,7 +82,7 @@ __device__ __forceinline__ void key_role(const BwdParams<T>& p, int bh, int kt, 
   using M = typename G::M;
   using KB = KeyBuf<T, HD, NW>;
   constexpr bool BF = G::BF;
-  constexpr int NB = G::NB, NDB = G::NDB, NC = G::NC, NU = G::NU, LD = G::LD;
+  constexpr int NB = G::NB, NDB = G::NDB, NC = G::NC, NU = G::NU;
   constexpr uint32_t ROWB = G::ROWB;
   constexpr int BKV = NW * 32;
 
@@ -100,7 +101,9 @@ __device__ __forceinline__ void key_role(const BwdParams<T>& p, int bh, int kt, 
   const int nm = p.causal ? min(nb, n0 + BKV / NB) : n0;
   const int nl = nb - 1;
 
-  auto buf = [&](int n) { return KB(smem + (size_t)(n & 3) * KB::BYTES); };
+  constexpr int NBUF = KB::NBUF;
+  auto buf = [&](int n) { return KB(smem + (size_t)((unsigned)n % NBUF) * KB::BYTES); };
+  const TileRead<T, HD, NW> rd;
 
   // this lane's key row of K and V: B operands of S = Q.K^T and dP = dO.V^T
   typename M::frag kf[NC], vf[NC];
@@ -131,18 +134,17 @@ __device__ __forceinline__ void key_role(const BwdParams<T>& p, int bh, int kt, 
   dma.init({make_desc(p.Q + hoff, head_bytes), make_desc(p.dO + hoff, head_bytes)},
            make_desc(p.Lse + (size_t)bh * S, (uint32_t)S * 4u), make_desc(p.Dl + (size_t)bh * S, (uint32_t)S * 4u));
   const uint32_t smem0 = lds_addr(smem);
-  auto fetch = [&](int n) { dma.issue(smem0 + (uint32_t)(n & 3) * KB::BYTES, n * NB); };
+  auto fetch = [&](int n) { dma.issue(smem0 + (uint32_t)((unsigned)n % NBUF) * KB::BYTES, n * NB); };
+  constexpr int AHEAD = NBUF - 3;   // blocks still in flight when a block is waited for
   // S and dP of block n: C tiles with column = this lane's key, rows = queries
   auto sdp = [&](int n, f32x16& s, f32x16& dp) {
     KB b = buf(n);
-    const T* qrow = b.q + (l & 31) * LD + M::KW * h;
-    const T* dorow = b.dO + (l & 31) * LD + M::KW * h;
     s = zero16();
     dp = zero16();
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      s = M::mma(ld_nat(qrow + c * M::KD), kf[c], s);
-      dp = M::mma(ld_nat(dorow + c * M::KD), vf[c], dp);
+      s = M::mma(rd.nat(b.q, c), kf[c], s);
+      dp = M::mma(rd.nat(b.dO, c), vf[c], dp);
     }
   };
 
@@ -178,8 +180,8 @@ __device__ __forceinline__ void key_role(const BwdParams<T>& p, int bh, int kt, 
 #pragma unroll
       for (int d = 0; d < NDB; ++d) {
         typename M::frag af, bf;
-        af = ld_res(b.dO, LD, 0, u, d * 32);
-        bf = ld_res(b.q, LD, 0, u, d * 32);
+        af = rd.tr(b.dO, u, d);
+        bf = rd.tr(b.q, u, d);
         dvacc[d] = M::mma(af, pf, dvacc[d]);
         dkacc[d] = M::mma(bf, sf, dkacc[d]);
       }
@@ -193,10 +195,9 @@ __device__ __forceinline__ void key_role(const BwdParams<T>& p, int bh, int kt, 
     settle(vf[c]);
   }
   f32x16 sa, pa, sb, pb;
-  fetch(n0);
-  fetch(n0 + 1);
-  fetch(n0 + 2);
-  wait_vm<NPW>();              // blocks n0, n0+1 landed; n0+2 in flight
+#pragma unroll
+  for (int i = 0; i < NBUF - 1; ++i) fetch(n0 + i);
+  wait_vm<AHEAD * NPW>();      // blocks n0, n0+1 landed, the rest in flight
   __syncthreads();
   sdp(n0, sa, pa);
   Pipe pipe(sa, pa, sb, pb);
@@ -207,13 +208,11 @@ __device__ __forceinline__ void key_role(const BwdParams<T>& p, int bh, int kt, 
   auto fused = [&](auto masked, auto par, int n) {
     if constexpr (BF) {
       constexpr int EPC = (16 + NC - 1) / NC;    // score elements finished per contraction step
-      fetch(n + 3);              // into the buffer of block n-1, finished before the last barrier
+      fetch(n + NBUF - 1);       // into the buffer of block n-1, finished before the last barrier
       KB bn = buf(n + 1), bc = buf(n);
       f32x16& sn = pipe.next(par).s;
       f32x16& dn = pipe.next(par).dp;
       f32x16 s = pipe.cur(par).s, dp = pipe.cur(par).dp;
-      const T* qrow = bn.q + (l & 31) * LD + M::KW * h;
-      const T* orow = bn.dO + (l & 31) * LD + M::KW * h;
       const int lo = kj - (n * NB + 4 * h);      // masked: query row rel sees key kj iff rel >= lo
       constexpr int NG = NU * NDB;               // gradient contraction pairs
       // LDS reads are spread over the contraction steps so that the matrix
@@ -231,12 +230,12 @@ __device__ __forceinline__ void key_role(const BwdParams<T>& p, int bh, int kt, 
         D4[g] = *reinterpret_cast<const f32x4*>(bc.D + 8 * g + 4 * h);
       };
       auto read_sc = [&](int c) {
-        qa[c] = ld_nat(qrow + c * M::KD);
-        oa[c] = ld_nat(orow + c * M::KD);
+        qa[c] = rd.nat(bn.q, c);
+        oa[c] = rd.nat(bn.dO, c);
       };
       auto read_tr = [&](int g) {
-        ta[g] = ld_res(bc.dO, LD, 0, g / NDB, (g % NDB) * 32);
-        tb[g] = ld_res(bc.q, LD, 0, g / NDB, (g % NDB) * 32);
+        ta[g] = rd.tr(bc.dO, g / NDB, g % NDB);
+        tb[g] = rd.tr(bc.q, g / NDB, g % NDB);
       };
       // row group g of L and D is first needed at step 4 g / EPC
 #pragma unroll
@@ -286,7 +285,7 @@ __device__ __forceinline__ void key_role(const BwdParams<T>& p, int bh, int kt, 
         if (g + NGA < NG) read_tr(g + NGA);
       }
       __builtin_amdgcn_sched_barrier(0);
-      wait_vm<NPW>();            // block n+2 landed; n+3 in flight
+      wait_vm<AHEAD * NPW>();    // block n+2 landed, later ones in flight
       __syncthreads();
     }
   };
@@ -294,10 +293,10 @@ __device__ __forceinline__ void key_role(const BwdParams<T>& p, int bh, int kt, 
     if constexpr (BF) {
       fused(masked, par, n);
     } else {
-      fetch(n + 3);            // into the buffer of block n-1, finished before the last barrier
+      fetch(n + NBUF - 1);     // into the buffer of block n-1, finished before the last barrier
       sdp(n + 1, pipe.next(par).s, pipe.next(par).dp);
       finish(masked, n, pipe.cur(par).s, pipe.cur(par).dp);
-      wait_vm<NPW>();          // block n+2 landed; n+3 in flight
+      wait_vm<AHEAD * NPW>();  // block n+2 landed, later ones in flight
       __syncthreads();
     }
   };
@@ -327,12 +326,13 @@ __device__ __forceinline__ void key_role(const BwdParams<T>& p, int bh, int kt, 
 }
 
 // ---------------------------------------------------------- query workgroups
-// One LDS buffer: row-major K and V blocks (row stride LD), as the DMA image
-// Dma<..., 2, false> lays them out.
+// One LDS buffer: the images of the K and V blocks, as Dma<..., 2, false>
+// lays them out.
 template <typename T, int HD, int NW>
 struct QueryBuf {
   using DM = Dma<T, HD, NW, 2, false>;
   static constexpr size_t BYTES = DM::BYTES;
+  static constexpr int NBUF = 4;   // rotating buffers (two bf16 workgroups fit per CU)
   T* k; T* v;
   __device__ QueryBuf(char* base) {
     k = reinterpret_cast<T*>(base);
@@ -346,7 +346,7 @@ __device__ __forceinline__ void query_role(const BwdParams<T>& p, int bh, int qq
   using M = typename G::M;
   using QB = QueryBuf<T, HD, NW>;
   constexpr bool BF = G::BF;
-  constexpr int NB = G::NB, NDB = G::NDB, NC = G::NC, NU = G::NU, LD = G::LD;
+  constexpr int NB = G::NB, NDB = G::NDB, NC = G::NC, NU = G::NU;
   constexpr uint32_t ROWB = G::ROWB;
   constexpr int BQ = NW * 32;
 
@@ -367,7 +367,9 @@ __device__ __forceinline__ void query_role(const BwdParams<T>& p, int bh, int qq
   const int nm = p.causal ? q0 / NB : nb;
   const int nl = nb - 1;
 
-  auto buf = [&](int n) { return QB(smem + (size_t)(n & 3) * QB::BYTES); };
+  constexpr int NBUF = QB::NBUF;
+  auto buf = [&](int n) { return QB(smem + (size_t)((unsigned)n % NBUF) * QB::BYTES); };
+  const TileRead<T, HD, NW> rd;
 
   // this lane's query row of Q and dO: B operands of S^T = K.Q^T and dP^T = V.dO^T
   typename M::frag qf[NC], of[NC];
@@ -397,19 +399,18 @@ __device__ __forceinline__ void query_role(const BwdParams<T>& p, int bh, int qq
   const u32x4s dK = make_desc(p.K + hoff, head_bytes);
   dma.init({dK, make_desc(p.V + hoff, head_bytes)}, dK, dK);
   const uint32_t smem0 = lds_addr(smem);
-  auto fetch = [&](int n) { dma.issue(smem0 + (uint32_t)(n & 3) * QB::BYTES, n * NB); };
+  auto fetch = [&](int n) { dma.issue(smem0 + (uint32_t)((unsigned)n % NBUF) * QB::BYTES, n * NB); };
+  constexpr int AHEAD = NBUF - 2;   // blocks still in flight when a block is waited for
 
   // S^T and dP^T of block n: C tiles with column = this lane's query, rows = keys
   auto sdp = [&](int n, f32x16& s, f32x16& dp) {
     QB b = buf(n);
-    const T* krow = b.k + (l & 31) * LD + M::KW * h;
-    const T* vrow = b.v + (l & 31) * LD + M::KW * h;
     s = zero16();
     dp = zero16();
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      s = M::mma(ld_nat(krow + c * M::KD), qf[c], s);
-      dp = M::mma(ld_nat(vrow + c * M::KD), of[c], dp);
+      s = M::mma(rd.nat(b.k, c), qf[c], s);
+      dp = M::mma(rd.nat(b.v, c), of[c], dp);
     }
   };
 
@@ -433,7 +434,7 @@ __device__ __forceinline__ void query_role(const BwdParams<T>& p, int bh, int qq
 #pragma unroll
       for (int d = 0; d < NDB; ++d) {
         typename M::frag af;
-        af = ld_res(b.k, LD, 0, u, d * 32);
+        af = rd.tr(b.k, u, d);
         dqacc[d] = M::mma(af, sf, dqacc[d]);
       }
     }
@@ -450,17 +451,16 @@ __device__ __forceinline__ void query_role(const BwdParams<T>& p, int bh, int qq
   // One block per iteration, score and gradient contractions back to back:
   // this kernel runs two waves per SIMD (it fits in half the register
   // file), and the other wave's work overlaps each wave's waits.
-  fetch(0);
-  fetch(1);
-  fetch(2);
-  wait_vm<2 * NPW>();          // block 0 landed; 1 and 2 in flight
+#pragma unroll
+  for (int i = 0; i < NBUF - 1; ++i) fetch(i);
+  wait_vm<AHEAD * NPW>();      // block 0 landed, the rest in flight
   __syncthreads();
   auto body = [&](auto masked, auto, int n) {
-    fetch(n + 3);              // into the buffer of block n-1, finished before the last barrier
+    fetch(n + NBUF - 1);       // into the buffer of block n-1, finished before the last barrier
     f32x16 s, dp;
     sdp(n, s, dp);
     finish(masked, n, s, dp);
-    wait_vm<2 * NPW>();        // block n+1 landed; n+2 and n+3 in flight
+    wait_vm<AHEAD * NPW>();    // block n+1 landed, later ones in flight
     __syncthreads();
   };
   // causal: blocks [0, nm) are unmasked and the rest cross the diagonal;
@@ -493,8 +493,8 @@ __device__ __forceinline__ void query_role(const BwdParams<T>& p, int bh, int qq
 template <typename T, int HD>
 struct BwdCfg {
   static constexpr int NW = 4;
-  static constexpr size_t KEY_BYTES = 4 * KeyBuf<T, HD, NW>::BYTES;     // four rotating buffers
-  static constexpr size_t QUERY_BYTES = 4 * QueryBuf<T, HD, NW>::BYTES;
+  static constexpr size_t KEY_BYTES = KeyBuf<T, HD, NW>::NBUF * KeyBuf<T, HD, NW>::BYTES;
+  static constexpr size_t QUERY_BYTES = QueryBuf<T, HD, NW>::NBUF * QueryBuf<T, HD, NW>::BYTES;
   static constexpr size_t SMEM = KEY_BYTES > QUERY_BYTES ? KEY_BYTES : QUERY_BYTES;
 };
 
