@@ -448,27 +448,93 @@ __device__ __forceinline__ void query_role(const BwdParams<T>& p, int bh, int qq
     settle(qf[c]);
     settle(of[c]);
   }
-  // One block per iteration, score and gradient contractions back to back:
-  // this kernel runs two waves per SIMD (it fits in half the register
-  // file), and the other wave's work overlaps each wave's waits.
-#pragma unroll
-  for (int i = 0; i < NBUF - 1; ++i) fetch(i);
-  wait_vm<AHEAD * NPW>();      // block 0 landed, the rest in flight
-  __syncthreads();
-  auto body = [&](auto masked, auto, int n) {
-    fetch(n + NBUF - 1);       // into the buffer of block n-1, finished before the last barrier
-    f32x16 s, dp;
-    sdp(n, s, dp);
-    finish(masked, n, s, dp);
-    wait_vm<AHEAD * NPW>();    // block n+1 landed, later ones in flight
-    __syncthreads();
-  };
   // causal: blocks [0, nm) are unmasked and the rest cross the diagonal;
   // non-causal: all are unmasked
   int n = 0, par = 0;
-  Pipe::run(body, std::false_type{}, n, min(nm, nl), par);
-  Pipe::run(body, std::true_type{}, n, nl, par);
-  {
+  if constexpr (BF) {
+    // As in the key workgroups: iteration n forms S^T and dP^T of block n+1
+    // while it finishes block n, with the LDS reads spread over the
+    // contraction steps (K and V rows of block n+1 PD steps ahead, the
+    // transposed K operands of block n NGA pairs during the score steps and
+    // the rest NGA ahead during the gradient steps).
+    constexpr int EPC = (16 + NC - 1) / NC;  // score elements finished per contraction step
+    constexpr int NG = NU * NDB;             // gradient contractions
+    constexpr int PD = 1;
+    constexpr int NGA = 2;
+#pragma unroll
+    for (int i = 0; i < NBUF - 1; ++i) fetch(i);
+    wait_vm<(NBUF - 3) * NPW>();   // blocks 0 and 1 landed, the rest in flight
+    __syncthreads();
+    f32x16 sa, pa, sb, pb;
+    sdp(0, sa, pa);
+    Pipe pipe(sa, pa, sb, pb);
+    auto body = [&](auto masked, auto par, int n) {
+      fetch(n + NBUF - 1);       // into the buffer of block n-1, finished before the last barrier
+      QB bn = buf(n + 1), bc = buf(n);
+      f32x16& sn = pipe.next(par).s;
+      f32x16& dn = pipe.next(par).dp;
+      f32x16 s = pipe.cur(par).s, dp = pipe.cur(par).dp;
+      const int rel = qi - (n * NB + 4 * h);   // masked: key row r is seen iff r <= rel
+      typename M::frag ka[NC], va[NC], ta[NG];
+      auto read_sc = [&](int c) {
+        ka[c] = rd.nat(bn.k, c);
+        va[c] = rd.nat(bn.v, c);
+      };
+      auto read_tr = [&](int g) { ta[g] = rd.tr(bc.k, g / NDB, g % NDB); };
+#pragma unroll
+      for (int c = 0; c < PD && c < NC; ++c) read_sc(c);
+      sn = zero16();
+      dn = zero16();
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        __builtin_amdgcn_sched_barrier(0);
+        sn = M::mma(ka[c], qf[c], sn);
+        dn = M::mma(va[c], of[c], dn);
+        if (c + PD < NC) read_sc(c + PD);
+#pragma unroll
+        for (int g = c * NGA / NC; g < (c + 1) * NGA / NC; ++g) read_tr(g);
+#pragma unroll
+        for (int v = c * EPC; v < (c + 1) * EPC && v < 16; ++v) {
+          const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[v], p.c_log2, -L2));
+          float ds = pr * (dp[v] - Di);
+          if constexpr (decltype(masked)::value) ds = (8 * (v >> 2) + (v & 3) > rel) ? 0.f : ds;
+          dp[v] = ds;
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      typename M::frag sf[NU];
+#pragma unroll
+      for (int u = 0; u < NU; ++u) sf[u] = frag_from_acc(dp, u, T{});
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        __builtin_amdgcn_sched_barrier(0);
+        dqacc[g % NDB] = M::mma(ta[g], sf[g / NDB], dqacc[g % NDB]);
+        if (g + NGA < NG) read_tr(g + NGA);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vm<(NBUF - 3) * NPW>();   // block n+2 landed, later ones in flight
+      __syncthreads();
+    };
+    Pipe::run(body, std::false_type{}, n, min(nm, nl), par);
+    Pipe::run(body, std::true_type{}, n, nl, par);
+    pipe.last(finish, nl >= nm, nl, par);
+  } else {
+    // fp32: one block per iteration, score and gradient contractions back
+    // to back
+#pragma unroll
+    for (int i = 0; i < NBUF - 1; ++i) fetch(i);
+    wait_vm<AHEAD * NPW>();      // block 0 landed, the rest in flight
+    __syncthreads();
+    auto body = [&](auto masked, auto, int n) {
+      fetch(n + NBUF - 1);       // into the buffer of block n-1, finished before the last barrier
+      f32x16 s, dp;
+      sdp(n, s, dp);
+      finish(masked, n, s, dp);
+      wait_vm<AHEAD * NPW>();    // block n+1 landed, later ones in flight
+      __syncthreads();
+    };
+    Pipe::run(body, std::false_type{}, n, min(nm, nl), par);
+    Pipe::run(body, std::true_type{}, n, nl, par);
     f32x16 s, dp;
     sdp(nl, s, dp);
     if (nl >= nm) finish(std::true_type{}, nl, s, dp);
