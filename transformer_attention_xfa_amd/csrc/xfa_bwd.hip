@@ -149,6 +149,7 @@ __device__ __forceinline__ void key_role(const BwdParams<T>& p, int bh, int kt, 
   };
 
   // p = 2^(s c - L log2 e), dS = p (dp - D); dV^T += dO^T.P, dK^T += Q^T.dS
+  // (a block's L is read as -L log2 e, see prescale)
   auto finish = [&](auto masked, int n, f32x16 s, f32x16 dp) {
     KB b = buf(n);
 #pragma unroll
@@ -158,7 +159,7 @@ __device__ __forceinline__ void key_role(const BwdParams<T>& p, int bh, int kt, 
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int v = 4 * g + e;
-        const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[v], p.c_log2, -L4[e] * kLog2e));
+        const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[v], p.c_log2, L4[e]));
         s[v] = pr;
         dp[v] = pr * (dp[v] - D4[e]);
       }
@@ -194,12 +195,21 @@ __device__ __forceinline__ void key_role(const BwdParams<T>& p, int bh, int kt, 
     settle(kf[c]);
     settle(vf[c]);
   }
+  // A block's L is rewritten in place as -L log2 e one iteration before its
+  // exponentials (the block has landed by then and nothing else reads its L
+  // in between): wave w takes rows 8w..8w+7, every lane of a group of eight
+  // writing the same value.  Split in two so the read has time to land.
+  const int lrow = 8 * w + (l & 7);
+  auto prescale_read = [&](int n) { return buf(n).L[lrow]; };
+  auto prescale_write = [&](int n, float x) { buf(n).L[lrow] = -x * kLog2e; };
   f32x16 sa, pa, sb, pb;
 #pragma unroll
   for (int i = 0; i < NBUF - 1; ++i) fetch(n0 + i);
   wait_vm<AHEAD * NPW>();      // blocks n0, n0+1 landed, the rest in flight
   __syncthreads();
+  prescale_write(n0, prescale_read(n0));
   sdp(n0, sa, pa);
+  __syncthreads();
   Pipe pipe(sa, pa, sb, pb);
   // bf16 iteration with the work interleaved by hand (sched_barrier fences
   // keep the order): the score contractions of block n+1 alternate with the
@@ -208,6 +218,7 @@ __device__ __forceinline__ void key_role(const BwdParams<T>& p, int bh, int kt, 
   auto fused = [&](auto masked, auto par, int n) {
     if constexpr (BF) {
       constexpr int EPC = (16 + NC - 1) / NC;    // score elements finished per contraction step
+      const float lx = prescale_read(n + 1);
       fetch(n + NBUF - 1);       // into the buffer of block n-1, finished before the last barrier
       KB bn = buf(n + 1), bc = buf(n);
       f32x16& sn = pipe.next(par).s;
@@ -258,7 +269,7 @@ __device__ __forceinline__ void key_role(const BwdParams<T>& p, int bh, int kt, 
         for (int g = c * NGA / NC; g < (c + 1) * NGA / NC; ++g) read_tr(g);
 #pragma unroll
         for (int v = c * EPC; v < (c + 1) * EPC && v < 16; ++v) {
-          const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[v], p.c_log2, -L4[v >> 2][v & 3] * kLog2e));
+          const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[v], p.c_log2, L4[v >> 2][v & 3]));
           float ps = pr, ds = pr * (dp[v] - D4[v >> 2][v & 3]);
           if constexpr (decltype(masked)::value) {
             const bool keep = 8 * (v >> 2) + (v & 3) >= lo;
@@ -270,6 +281,7 @@ __device__ __forceinline__ void key_role(const BwdParams<T>& p, int bh, int kt, 
         }
       }
       __builtin_amdgcn_sched_barrier(0);
+      prescale_write(n + 1, lx);
       typename M::frag pf[NU], sf[NU];
 #pragma unroll
       for (int u = 0; u < NU; ++u) {
@@ -293,6 +305,7 @@ __device__ __forceinline__ void key_role(const BwdParams<T>& p, int bh, int kt, 
     if constexpr (BF) {
       fused(masked, par, n);
     } else {
+      prescale_write(n + 1, prescale_read(n + 1));
       fetch(n + NBUF - 1);     // into the buffer of block n-1, finished before the last barrier
       sdp(n + 1, pipe.next(par).s, pipe.next(par).dp);
       finish(masked, n, pipe.cur(par).s, pipe.cur(par).dp);
