@@ -211,19 +211,42 @@ __device__ __forceinline__ void key_role(const BwdParams<T>& p, int bh, int kt, 
   sdp(n0, sa, pa);
   __syncthreads();
   Pipe pipe(sa, pa, sb, pb);
+  // bf16: the u = 1 gradient contractions of a block run at the start of the
+  // next iteration, their operands carried in registers across the barrier,
+  // so the matrix core has work while that iteration's first LDS reads land.
+  // The carried operands start as zeros (contractions that add nothing).
+  // Carried: the transposed dO and Q operands of u = 1 and the u = 1
+  // fragments of P and dS.
+  typename M::frag cta[NDB], ctb[NDB], cpf{}, csf{};
+#pragma unroll
+  for (int d = 0; d < NDB; ++d) {
+    cta[d] = typename M::frag{};
+    ctb[d] = typename M::frag{};
+  }
+  auto carried = [&]() {
+#pragma unroll
+    for (int d = 0; d < NDB; ++d) {
+      dvacc[d] = M::mma(cta[d], cpf, dvacc[d]);
+      dkacc[d] = M::mma(ctb[d], csf, dkacc[d]);
+    }
+  };
   // bf16 iteration with the work interleaved by hand (sched_barrier fences
   // keep the order): the score contractions of block n+1 alternate with the
   // exponentials and dS of block n and the reads of block n's gradient
   // operands.  Same arithmetic as sdp() then finish().
   auto fused = [&](auto masked, auto par, int n) {
     if constexpr (BF) {
+      static_assert(NU == 2, "bf16 contraction steps are 16 deep");
       constexpr int EPC = (16 + NC - 1) / NC;    // score elements finished per contraction step
       const float lx = prescale_read(n + 1);
       fetch(n + NBUF - 1);       // into the buffer of block n-1, finished before the last barrier
       KB bn = buf(n + 1), bc = buf(n);
       f32x16& sn = pipe.next(par).s;
       f32x16& dn = pipe.next(par).dp;
-      f32x16 s = pipe.cur(par).s, dp = pipe.cur(par).dp;
+      // scores of block n (read in place) and its P and dS
+      const f32x16& s = pipe.cur(par).s;
+      const f32x16& dp = pipe.cur(par).dp;
+      f32x16 ps, ds;
       const int lo = kj - (n * NB + 4 * h);      // masked: query row rel sees key kj iff rel >= lo
       constexpr int NG = NU * NDB;               // gradient contraction pairs
       // LDS reads are spread over the contraction steps so that the matrix
@@ -234,7 +257,7 @@ __device__ __forceinline__ void key_role(const BwdParams<T>& p, int bh, int kt, 
       // and the rest NGA pairs ahead during the gradient steps.
       constexpr int PD = 2;
       constexpr int NGA = NG / 2;
-      typename M::frag qa[NC], oa[NC], ta[NG], tb[NG];
+      typename M::frag qa[NC], oa[NC], ta[NDB], tb[NDB];
       f32x4 L4[4], D4[4];
       auto read_ld = [&](int g) {
         L4[g] = *reinterpret_cast<const f32x4*>(bc.L + 8 * g + 4 * h);
@@ -244,16 +267,57 @@ __device__ __forceinline__ void key_role(const BwdParams<T>& p, int bh, int kt, 
         qa[c] = rd.nat(bn.q, c);
         oa[c] = rd.nat(bn.dO, c);
       };
+      // u = 0 operands into ta/tb, u = 1 operands straight into the carried set
       auto read_tr = [&](int g) {
-        ta[g] = rd.tr(bc.dO, g / NDB, g % NDB);
-        tb[g] = rd.tr(bc.q, g / NDB, g % NDB);
+        if (g < NDB) {
+          ta[g] = rd.tr(bc.dO, 0, g);
+          tb[g] = rd.tr(bc.q, 0, g);
+        } else {
+          cta[g - NDB] = rd.tr(bc.dO, 1, g - NDB);
+          ctb[g - NDB] = rd.tr(bc.q, 1, g - NDB);
+        }
       };
-      // row group g of L and D is first needed at step 4 g / EPC
+      // The exponentials are spread over all the contraction steps, since a
+      // wave's vector instructions overlap its own matrix instructions only
+      // up to a few per contraction: the elements of the u = 0 fragment
+      // (0..7) during the score steps, the others during the u = 0 gradient
+      // steps, so each fragment is complete when its contractions start.
+      // Steps are numbered 0..NC-1 (score), NC..NC+NG-1 (gradient).
+      constexpr int SPLIT = 8;
+      constexpr int EA = (SPLIT + NC - 1) / NC;          // elements per score step
+      constexpr int EB = (16 - SPLIT + NDB - 1) / NDB;   // elements per u = 0 gradient step
+      auto fin_step = [](int v) { return v < SPLIT ? v / EA : NC + (v - SPLIT) / EB; };
+      // row group g of L and D is read one step before its first element
+      auto ld_step = [&](int g) { return fin_step(4 * g) - 1; };
+      auto softmax = [&](int v) {
+        const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[v], p.c_log2, L4[v >> 2][v & 3]));
+        float pv = pr, dv = pr * (dp[v] - D4[v >> 2][v & 3]);
+        if constexpr (decltype(masked)::value) {
+          const bool keep = 8 * (v >> 2) + (v & 3) >= lo;
+          pv = keep ? pv : 0.f;
+          dv = keep ? dv : 0.f;
+        }
+        // pinned here: otherwise the compiler sinks the arithmetic to the
+        // fragment conversion, bunching it where no contraction overlaps it
+        settle(pv);
+        settle(dv);
+        ps[v] = pv;
+        ds[v] = dv;
+      };
+      auto step_extras = [&](int st) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          if (ld_step(g) == st) read_ld(g);
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          if (fin_step(v) == st) softmax(v);
+      };
 #pragma unroll
       for (int g = 0; g < 4; ++g)
-        if (4 * g / EPC == 0) read_ld(g);
+        if (ld_step(g) < 0) read_ld(g);
 #pragma unroll
       for (int c = 0; c < PD && c < NC; ++c) read_sc(c);
+      carried();                 // block n-1, u = 1
       sn = zero16();
       dn = zero16();
 #pragma unroll
@@ -263,39 +327,23 @@ __device__ __forceinline__ void key_role(const BwdParams<T>& p, int bh, int kt, 
         dn = M::mma(oa[c], vf[c], dn);
         if (c + PD < NC) read_sc(c + PD);
 #pragma unroll
-        for (int g = 1; g < 4; ++g)
-          if (4 * g / EPC == c + 1) read_ld(g);
-#pragma unroll
         for (int g = c * NGA / NC; g < (c + 1) * NGA / NC; ++g) read_tr(g);
-#pragma unroll
-        for (int v = c * EPC; v < (c + 1) * EPC && v < 16; ++v) {
-          const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[v], p.c_log2, L4[v >> 2][v & 3]));
-          float ps = pr, ds = pr * (dp[v] - D4[v >> 2][v & 3]);
-          if constexpr (decltype(masked)::value) {
-            const bool keep = 8 * (v >> 2) + (v & 3) >= lo;
-            ps = keep ? ps : 0.f;
-            ds = keep ? ds : 0.f;
-          }
-          s[v] = ps;
-          dp[v] = ds;
-        }
+        step_extras(c);
       }
       __builtin_amdgcn_sched_barrier(0);
       prescale_write(n + 1, lx);
-      typename M::frag pf[NU], sf[NU];
+      const typename M::frag pf = frag_from_acc(ps, 0, T{}), sf = frag_from_acc(ds, 0, T{});
 #pragma unroll
-      for (int u = 0; u < NU; ++u) {
-        pf[u] = frag_from_acc(s, u, T{});
-        sf[u] = frag_from_acc(dp, u, T{});
-      }
-#pragma unroll
-      for (int g = 0; g < NG; ++g) {
+      for (int d = 0; d < NDB; ++d) {
         __builtin_amdgcn_sched_barrier(0);
-        const int u = g / NDB, d = g % NDB;
-        dvacc[d] = M::mma(ta[g], pf[u], dvacc[d]);
-        dkacc[d] = M::mma(tb[g], sf[u], dkacc[d]);
-        if (g + NGA < NG) read_tr(g + NGA);
+        dvacc[d] = M::mma(ta[d], pf, dvacc[d]);
+        dkacc[d] = M::mma(tb[d], sf, dkacc[d]);
+        if (d + NGA < NG) read_tr(d + NGA);
+        step_extras(NC + d);
       }
+      __builtin_amdgcn_sched_barrier(0);
+      cpf = frag_from_acc(ps, 1, T{});   // u = 1: carried into the next iteration
+      csf = frag_from_acc(ds, 1, T{});
       __builtin_amdgcn_sched_barrier(0);
       wait_vm<AHEAD * NPW>();    // block n+2 landed, later ones in flight
       __syncthreads();
@@ -318,6 +366,7 @@ __device__ __forceinline__ void key_role(const BwdParams<T>& p, int bh, int kt, 
   int n = n0, par = 0;
   pipe.run(body, std::true_type{}, n, min(nm, nl), par);
   pipe.run(body, std::false_type{}, n, nl, par);
+  if constexpr (BF) carried();  // the last carried block
   pipe.last(finish, nl < nm, nl, par);
   wait_vm<0>();                // the fetches of blocks past the end write LDS: drain them
 
