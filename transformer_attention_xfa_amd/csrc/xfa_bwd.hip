@@ -237,7 +237,6 @@ __device__ __forceinline__ void key_role(const BwdParams<T>& p, int bh, int kt, 
   auto fused = [&](auto masked, auto par, int n) {
     if constexpr (BF) {
       static_assert(NU == 2, "bf16 contraction steps are 16 deep");
-      constexpr int EPC = (16 + NC - 1) / NC;    // score elements finished per contraction step
       const float lx = prescale_read(n + 1);
       fetch(n + NBUF - 1);       // into the buffer of block n-1, finished before the last barrier
       KB bn = buf(n + 1), bc = buf(n);
