@@ -116,3 +116,12 @@ def test_op_rejects_host_tensors():
     q = torch.zeros(1, 1, 8, 16)
     with pytest.raises(ValueError, match="GPU"):
         xfa.flash_attention(q, q, q)
+
+
+def test_flash_attention_rejects_unknown_core():
+    import torch
+    import transformer_attention_xfa_amd as xfa
+    t = torch.zeros(1, 1, 4, 16)
+    with pytest.raises(ValueError):
+        xfa.flash_attention(t, t, t, core="fp16")
+    assert xfa.CORES == ("native", "fp32")

@@ -117,3 +117,43 @@ def test_peak_memory_flash_vs_composed():
     # and both compute the same thing
     for a, b in zip(res["composed"], res["flash"]):
         assert torch.allclose(a, b, atol=2e-4, rtol=2e-4), (a - b).abs().max().item()
+
+
+@pytest.mark.parametrize("B,H,S,hd,causal", [(1, 2, 300, 128, True), (2, 1, 129, 64, False)])
+def test_fp32_core_mode(B, H, S, hd, causal):
+    """core="fp32" on bf16 tensors (the pages' numerics: casts at the
+    boundary, fp32 kernels inside) against the oracle on the same bf16
+    inputs.  Only the bf16 rounding of out and of the gradients remains, so
+    its errors are within a few bf16 ulps and no larger than the native
+    bf16 path's, which also rounds P and dS to bf16."""
+    w = workloads.Workload(f"core_{S}_{hd}", "bf16", B, H, S, hd, seed=12, causal=causal)
+    x = workloads.make_inputs(w)
+    say(f"fp32 core {w.name} B={B} H={H} causal={causal}")
+
+    def dev(n):
+        return torch.from_numpy(getattr(x, n + "_bits").view(np.int16)).view(torch.bfloat16).cuda()
+
+    errs = {}
+    for core in ("fp32", "native"):
+        q, k, v = (dev(n).requires_grad_(True) for n in ("q", "k", "v"))
+        out = xfa.flash_attention(q, k, v, causal=causal, core=core)
+        assert out.dtype == torch.bfloat16
+        grads = torch.autograd.grad(out, (q, k, v), grad_outputs=dev("do"))
+        e = dict(out=0.0, dq=0.0, dk=0.0, dv=0.0)
+        for bh in range(w.BH):
+            b_, h_ = divmod(bh, H)
+            args = [x.f64(n, bh) for n in ("q", "k", "v")]
+            o_r, _ = attention_forward_head(*args, w.sm_scale, causal)
+            refs = attention_backward_head(*args, x.f64("do", bh), w.sm_scale, causal)[:3]
+            e["out"] = max(e["out"], float(np.abs(out[b_, h_].detach().float().cpu().numpy() - o_r).max()))
+            for name, got, ref in zip(("dq", "dk", "dv"), grads, refs):
+                g = got[b_, h_].float().cpu().numpy()
+                e[name] = max(e[name], float(np.abs(g - ref).max() / max(np.abs(ref).max(), 1e-2)))
+        errs[core] = e
+        say(f"  core={core}: " + ", ".join(f"{k_} {v_:.3g}" for k_, v_ in e.items()))
+    # bf16 has an 8-bit significand: one rounding is at most 2^-9 relative
+    assert errs["fp32"]["out"] <= 2.0 ** -7 * 4, errs["fp32"]
+    for name in ("dq", "dk", "dv"):
+        assert errs["fp32"][name] <= 2.0 ** -7, (name, errs["fp32"])
+    for name in errs["fp32"]:
+        assert errs["fp32"][name] <= errs["native"][name] * 1.05 + 1e-6, (name, errs)

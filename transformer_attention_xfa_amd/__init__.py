@@ -22,4 +22,4 @@ from ._binding import (  # noqa: F401
     xfa_status_string,
 )
 
-from .autograd import FlashAttentionFn, flash_attention  # noqa: E402,F401
+from .autograd import CORES, FlashAttentionFn, flash_attention  # noqa: E402,F401
