@@ -1,6 +1,6 @@
 """Throughput of the fused causal attention path on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--comparator]
 
 One step is one pass of the whole path over one batch: xfa_fwd, then
 xfa_bwd_preprocess, then xfa_bwd, with inputs resident in HBM.  The default
@@ -9,7 +9,9 @@ JSON line carries the whole-step throughput in algorithmic TFLOP/s (only
 unmasked query/key pairs count: 4*hd flop per pair forward, 10*hd backward),
 each kernel's average duration from HIP events recorded on the stream the
 kernels run on, the roofline of the dominant kernel, and the CPU oracle timed
-on a bounded sample of the same workload.
+on a bounded sample of the same workload.  --comparator adds composed
+attention (comparator.py) on the same inputs: its time and both paths' peak
+memory.
 """
 
 from __future__ import annotations
@@ -156,6 +158,8 @@ def main(argv=None):
     ap.add_argument("--workload", default=workloads.C4.name, choices=sorted(workloads.BY_NAME))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=32)
+    ap.add_argument("--comparator", action="store_true",
+                    help="also time composed attention (library GEMMs + softmax) and both paths' peak memory")
     args = ap.parse_args(argv)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -213,6 +217,9 @@ def main(argv=None):
         "phases": phases,
         "device": device,
     }
+    if args.comparator:
+        import comparator
+        rec["comparator"] = comparator.comparator_record(x, max(1, args.steps // 4), 1, ms_step)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(x, args.cpu_heads)
     print(json.dumps(rec), flush=True)

@@ -1,0 +1,127 @@
+"""The composed attention path on MI355X, as a benchmark comparator for the
+fused op (T14 flash-attention design doc: the composed path the fused kernel
+replaces, and its measured-results section, which compares the two on
+throughput and peak memory).
+
+Composed attention materialises the scores: S = Q K^T * scale by a batched
+GEMM, the causal mask and a softmax writing the [B, H, S, S] probabilities P,
+out = P V by a second GEMM; the backward keeps P and forms dV, dP, dS, dQ, dK
+with three more GEMMs and elementwise work on S x S tensors.  The GEMMs and
+the softmax are library kernels (torch on ROCm: hipBLASLt and its softmax);
+this is a comparator, not a second implementation of the op, and it computes
+all S*S products where the fused op skips the masked half.  Every batched
+product is given contiguous operands (the transposes are formed as small
+[.., hd, S] copies), and the softmax runs in fp32.
+"""
+
+from __future__ import annotations
+
+import time
+
+import numpy as np
+
+
+def composed_forward(q, k, v, scale, causal):
+    """out, P for [B, H, S, hd] q, k, v (P kept for the backward)."""
+    import torch
+
+    s = torch.matmul(q, k.transpose(-1, -2).contiguous())
+    s = s.float() * scale
+    if causal:
+        S = q.shape[-2]
+        mask = torch.ones(S, S, dtype=torch.bool, device=q.device).triu(1)
+        s.masked_fill_(mask, float("-inf"))
+    p = torch.softmax(s, dim=-1).to(q.dtype)
+    del s
+    return torch.matmul(p, v), p
+
+
+def composed_backward(q, k, v, p, out, do, scale):
+    """dq, dk, dv of sum(do * out) from the kept probabilities p."""
+    import torch
+
+    dv = torch.matmul(do.transpose(-1, -2).contiguous(), p).transpose(-1, -2)      # (dO^T P)^T = P^T dO
+    dp = torch.matmul(do, v.transpose(-1, -2).contiguous()).float()
+    delta = (do.float() * out.float()).sum(-1, keepdim=True)
+    ds = (p.float() * (dp - delta) * scale).to(q.dtype)
+    del dp
+    dq = torch.matmul(ds, k)
+    dk = torch.matmul(q.transpose(-1, -2).contiguous(), ds).transpose(-1, -2)     # (Q^T dS)^T = dS^T Q
+    return dq, dk.contiguous(), dv.contiguous()
+
+
+def bench_composed(q, k, v, do, scale, causal, steps, warmup):
+    """Average fwd and bwd times (HIP events on the current stream) and the
+    peak memory above the inputs of one fwd + bwd step, for the composed path
+    and for the fused op (its outputs and O(S) buffers allocated inside the
+    measured step the same way)."""
+    import torch
+
+    import transformer_attention_xfa_amd as xfa
+
+    stream = torch.cuda.current_stream()
+
+    def composed_step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        out, p = composed_forward(q, k, v, scale, causal)
+        if ev is not None:
+            ev[1].record(stream)
+        grads = composed_backward(q, k, v, p, out, do, scale)
+        if ev is not None:
+            ev[2].record(stream)
+        return out, grads
+
+    def fused_step():
+        out, lse = xfa.forward(q, k, v, scale, causal)
+        return out, xfa.backward(q, k, v, out, do, lse, scale, causal)
+
+    def peak(fn):
+        torch.cuda.synchronize()
+        torch.cuda.reset_peak_memory_stats()
+        base = torch.cuda.memory_allocated()
+        r = fn()
+        torch.cuda.synchronize()
+        p_ = torch.cuda.max_memory_allocated() - base
+        del r
+        return p_
+
+    for _ in range(warmup):
+        composed_step()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        composed_step(events[i])
+    torch.cuda.synchronize()
+    fwd = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
+    bwd = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
+    peak_c = peak(composed_step)
+    peak_f = peak(fused_step)
+    return {"fwd_ms": fwd, "bwd_ms": bwd, "peak_bytes": int(peak_c), "fused_peak_bytes": int(peak_f)}
+
+
+def comparator_record(x, steps, warmup, fused_ms_step):
+    """The comparator object of bench.py's JSON line for inputs x."""
+    import torch
+
+    w = x.w
+    dev = torch.device("cuda", 0)
+    if w.dtype == "bf16":
+        q, k, v, do = (torch.from_numpy(getattr(x, n + "_bits").view(np.int16)).view(torch.bfloat16).to(dev)
+                       for n in ("q", "k", "v", "do"))
+    else:
+        q, k, v, do = (torch.from_numpy(getattr(x, n)).to(dev) for n in ("q", "k", "v", "do"))
+    t0 = time.perf_counter()
+    r = bench_composed(q, k, v, do, w.sm_scale, w.causal, steps, warmup)
+    flop = w.fwd_flop + w.bwd_flop
+    ms = r["fwd_ms"] + r["bwd_ms"]
+    return {
+        "kind": "composed attention (library GEMMs and softmax, [B,H,S,S] probabilities kept for the backward)",
+        "fwd_ms": round(r["fwd_ms"], 3), "bwd_ms": round(r["bwd_ms"], 3), "ms_per_step": round(ms, 3),
+        "value": round(flop / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+        "note": "same algorithmic flop count as the fused op; the composed path computes all S*S products",
+        "speedup_fused": round(ms / fused_ms_step, 2),
+        "peak_mib_composed": round(r["peak_bytes"] / 2**20, 1),
+        "peak_mib_fused": round(r["fused_peak_bytes"] / 2**20, 1),
+        "seconds": round(time.perf_counter() - t0, 1),
+    }
