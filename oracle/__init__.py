@@ -17,3 +17,9 @@ from .attention import (  # noqa: F401
     attention_forward_head,
     attention_forward_rows,
 )
+from .dropout import (  # noqa: F401
+    attention_dropout_backward_head,
+    attention_dropout_forward_head,
+    keep_mask,
+    splitmix64,
+)
