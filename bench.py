@@ -1,6 +1,7 @@
 """Throughput of the fused causal attention path on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--comparator]
+                    [--dropout P]
 
 One step is one pass of the whole path over one batch: xfa_fwd, then
 xfa_bwd_preprocess, then xfa_bwd, with inputs resident in HBM.  The default
@@ -11,7 +12,9 @@ each kernel's average duration from HIP events recorded on the stream the
 kernels run on, the roofline of the dominant kernel, and the CPU oracle timed
 on a bounded sample of the same workload.  --comparator adds composed
 attention (comparator.py) on the same inputs: its time and both paths' peak
-memory.
+memory.  --dropout P adds the same step with dropout on the attention
+probabilities (xfa_fwd_dropout / xfa_bwd_dropout) and its cost over the plain
+step; the headline value is always the plain step.
 """
 
 from __future__ import annotations
@@ -65,7 +68,7 @@ def measured_traffic(phase: str, w) -> float | None:
     return float(rec["hbm_bytes_per_launch"])
 
 
-def gpu_bench(x, steps: int, warmup: int):
+def gpu_bench(x, steps: int, warmup: int, dropout_p: float = 0.0, seed: int = 0x5EED):
     import torch
 
     import transformer_attention_xfa_amd as xfa
@@ -89,13 +92,19 @@ def gpu_bench(x, steps: int, warmup: int):
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        xfa.xfa_fwd(q, k, v, out, lse, scale, causal, stream)
+        if dropout_p:
+            xfa.xfa_fwd_dropout(q, k, v, out, lse, scale, causal, dropout_p, seed, stream)
+        else:
+            xfa.xfa_fwd(q, k, v, out, lse, scale, causal, stream)
         if ev is not None:
             ev[1].record(stream)
         xfa.xfa_bwd_preprocess(out, do, delta, scale, causal, stream)
         if ev is not None:
             ev[2].record(stream)
-        xfa.xfa_bwd(q, k, v, do, lse, delta, dq, dk, dv, scale, causal, stream)
+        if dropout_p:
+            xfa.xfa_bwd_dropout(q, k, v, do, lse, delta, dq, dk, dv, scale, causal, dropout_p, seed, stream)
+        else:
+            xfa.xfa_bwd(q, k, v, do, lse, delta, dq, dk, dv, scale, causal, stream)
         if ev is not None:
             ev[3].record(stream)
 
@@ -160,7 +169,11 @@ def main(argv=None):
     ap.add_argument("--cpu-heads", type=int, default=32)
     ap.add_argument("--comparator", action="store_true",
                     help="also time composed attention (library GEMMs + softmax) and both paths' peak memory")
+    ap.add_argument("--dropout", type=float, default=0.0, metavar="P",
+                    help="also time the step with dropout probability P on the attention probabilities")
     args = ap.parse_args(argv)
+    if not 0.0 <= args.dropout < 1.0:
+        ap.error("--dropout must be in [0, 1)")
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: the attention path is independent per head, and "
@@ -217,6 +230,16 @@ def main(argv=None):
         "phases": phases,
         "device": device,
     }
+    if args.dropout:
+        d_step, d_mean, _, _ = gpu_bench(x, args.steps, args.warmup, dropout_p=args.dropout)
+        rec["dropout"] = {
+            "p": args.dropout, "kernels": "fwd_kernel, bwd_key_kernel + bwd_query_kernel with in-kernel keep bits",
+            "ms_per_step": round(d_step, 4), "fwd_ms": round(d_mean["fwd"], 4), "bwd_ms": round(d_mean["bwd"], 4),
+            "value": round(flop / (d_step * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+            "step_cost_vs_plain": round(d_step / ms_step, 3),
+            "fwd_cost_vs_plain": round(d_mean["fwd"] / ms_mean["fwd"], 3),
+            "bwd_cost_vs_plain": round(d_mean["bwd"] / ms_mean["bwd"], 3),
+        }
     if args.comparator:
         import comparator
         rec["comparator"] = comparator.comparator_record(x, max(1, args.steps // 4), 1, ms_step)

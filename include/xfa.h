@@ -98,6 +98,33 @@ xfa_status_t xfa_bwd(const void* q, const void* k, const void* v, const void* do
                      int64_t B, int64_t H, int64_t S, int64_t hd, float scale, int causal,
                      int dtype, void* stream);
 
+/* Dropout on the attention probabilities (xtrain dropout design doc, section
+ * "RNG: counter-based"; applied to P as inverted dropout): with
+ * M_ij = keep_ij / (1 - p),  out = (P o M) V  and L unchanged.  Element
+ * (head bh, query i, key j) has flat index n = (bh*S + i)*S + j and
+ *   keep = (splitmix64(seed XOR (n * 0x9E3779B97F4A7C15 mod 2^64)) >> 40)
+ *          >= ceil(p * 2^24),
+ * which is the doc's float32 test (top 24 bits / 2^24 >= p); splitmix64(x)
+ * is one step of Steele, Lea and Flood's generator from state x.  The mask
+ * depends on (seed, n) only and is regenerated in the backward, never
+ * stored.  The backward (same doc, "dropout node backward", by the chain
+ * rule): dV = (P o M)^T dO, dP = M o (dO V^T), ds = p (dP - D) scale;
+ * D = rowsum(dO * out) from xfa_bwd_preprocess on the dropped out is still
+ * rowsum(P o dP), so the preprocess is unchanged.
+ *   dropout_p  in [0, 1), finite; else XFA_ERR_INVALID_ARGUMENT.  p = 0
+ *              runs the kernels without dropout (bitwise the plain calls).
+ *   seed       any 64-bit value; the forward and the backward of one step
+ *              must get the same seed, p, B, H, S.
+ * Other arguments, layouts and errors as in xfa_fwd and xfa_bwd.            */
+xfa_status_t xfa_fwd_dropout(const void* q, const void* k, const void* v, void* out, float* lse,
+                             int64_t B, int64_t H, int64_t S, int64_t hd, float scale, int causal,
+                             float dropout_p, uint64_t seed, int dtype, void* stream);
+
+xfa_status_t xfa_bwd_dropout(const void* q, const void* k, const void* v, const void* dout,
+                             const float* lse, const float* delta, void* dq, void* dk, void* dv,
+                             int64_t B, int64_t H, int64_t S, int64_t hd, float scale, int causal,
+                             float dropout_p, uint64_t seed, int dtype, void* stream);
+
 /* Static, NUL-terminated description of a status code.                       */
 const char* xfa_status_string(xfa_status_t status);
 

@@ -24,7 +24,8 @@ def _declared():
 
 def test_library_exports_every_declared_symbol():
     names = _declared()
-    assert names == sorted(["xfa_fwd", "xfa_bwd_preprocess", "xfa_bwd", "xfa_status_string"])
+    assert names == sorted(["xfa_fwd", "xfa_bwd_preprocess", "xfa_bwd", "xfa_fwd_dropout", "xfa_bwd_dropout",
+                            "xfa_status_string"])
     lib = ctypes.CDLL(xfa.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -59,7 +60,23 @@ def _bwd(**kw):
                              a["causal"], a["dtype"], None)
 
 
-@pytest.mark.parametrize("call", [_fwd, _pre, _bwd])
+def _fwd_drop(**kw):
+    a = dict(q=A, k=A, v=A, out=A, lse=A, B=1, H=2, S=64, hd=64, scale=0.125, causal=1, p=0.1, seed=7, dtype=1)
+    a.update(kw)
+    return xfa.lib().xfa_fwd_dropout(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"], a["H"], a["S"],
+                                     a["hd"], a["scale"], a["causal"], a["p"], a["seed"], a["dtype"], None)
+
+
+def _bwd_drop(**kw):
+    a = dict(q=A, k=A, v=A, dout=A, lse=A, delta=A, dq=A, dk=A, dv=A,
+             B=1, H=2, S=64, hd=64, scale=0.125, causal=1, p=0.1, seed=7, dtype=1)
+    a.update(kw)
+    return xfa.lib().xfa_bwd_dropout(a["q"], a["k"], a["v"], a["dout"], a["lse"], a["delta"], a["dq"],
+                                     a["dk"], a["dv"], a["B"], a["H"], a["S"], a["hd"], a["scale"],
+                                     a["causal"], a["p"], a["seed"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("call", [_fwd, _pre, _bwd, _fwd_drop, _bwd_drop])
 def test_rejects_bad_arguments(call):
     assert call(dtype=2) == INVAL
     assert call(dtype=-1) == INVAL
@@ -81,6 +98,8 @@ def test_rejects_bad_arguments(call):
     (_fwd, ["q", "k", "v", "out", "lse"]),
     (_pre, ["out", "dout", "delta"]),
     (_bwd, ["q", "k", "v", "dout", "lse", "delta", "dq", "dk", "dv"]),
+    (_fwd_drop, ["q", "k", "v", "out", "lse"]),
+    (_bwd_drop, ["q", "k", "v", "dout", "lse", "delta", "dq", "dk", "dv"]),
 ])
 def test_rejects_null_and_misaligned_pointers(call, ptrs):
     for p in ptrs:
@@ -98,11 +117,24 @@ def test_size_limits():
         assert _bwd(S=1 << 23, hd=64, dtype=dtype) == UNSUP
 
 
-@pytest.mark.parametrize("call", [_fwd, _pre, _bwd])
+@pytest.mark.parametrize("call", [_fwd_drop, _bwd_drop])
+def test_dropout_rejects_bad_probability(call):
+    # p must lie in [0, 1); p = 1 would drop everything and divide by zero
+    for p in (-0.1, -1e-30, 1.0, 1.5, math.nan, math.inf, -math.inf):
+        assert call(p=p) == INVAL, p
+    # the probability is checked before the pointers: nothing valid is needed
+    assert call(p=1.0, q=None) == INVAL
+    # any 64-bit seed is accepted (an empty problem returns before launching)
+    for seed in (0, 1, (1 << 64) - 1, 0x9E3779B97F4A7C15):
+        assert call(seed=seed, S=0) == OK
+
+
+@pytest.mark.parametrize("call", [_fwd, _pre, _bwd, _fwd_drop, _bwd_drop])
 def test_empty_problem_is_a_no_op(call):
     # nothing to do: succeeds without touching (null) pointers or the GPU
     nulls = {"fwd": ["q", "k", "v", "out", "lse"], "pre": ["out", "dout", "delta"],
              "bwd": ["q", "k", "v", "dout", "lse", "delta", "dq", "dk", "dv"]}
+    nulls["fwd_drop"], nulls["bwd_drop"] = nulls["fwd"], nulls["bwd"]
     key = call.__name__[1:]
     args = {p: None for p in nulls[key]}
     assert call(S=0, **args) == OK
@@ -125,3 +157,11 @@ def test_flash_attention_rejects_unknown_core():
     with pytest.raises(ValueError):
         xfa.flash_attention(t, t, t, core="fp16")
     assert xfa.CORES == ("native", "fp32")
+
+
+@pytest.mark.parametrize("p", [-0.5, 1.0, 2.0])
+def test_flash_attention_rejects_bad_dropout_probability(p):
+    import torch
+    t = torch.zeros(1, 1, 4, 16)
+    with pytest.raises(ValueError, match="dropout_p"):
+        xfa.flash_attention(t, t, t, dropout_p=p)

@@ -17,8 +17,10 @@ from ._binding import (  # noqa: F401
     forward,
     lib,
     xfa_bwd,
+    xfa_bwd_dropout,
     xfa_bwd_preprocess,
     xfa_fwd,
+    xfa_fwd_dropout,
     xfa_status_string,
 )
 

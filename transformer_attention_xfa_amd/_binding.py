@@ -21,11 +21,13 @@ XFA_ERR_UNSUPPORTED = 2
 XFA_ERR_HIP = 3
 
 # exported symbols and their C signatures (mirrors include/xfa.h)
-_c_void_p, _i64, _f32, _int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int
+_c_void_p, _i64, _f32, _int, _u64 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int, ctypes.c_uint64
 _SIGS = {
     "xfa_fwd": (_int, [_c_void_p] * 5 + [_i64] * 4 + [_f32, _int, _int, _c_void_p]),
     "xfa_bwd_preprocess": (_int, [_c_void_p] * 3 + [_i64] * 4 + [_f32, _int, _int, _c_void_p]),
     "xfa_bwd": (_int, [_c_void_p] * 9 + [_i64] * 4 + [_f32, _int, _int, _c_void_p]),
+    "xfa_fwd_dropout": (_int, [_c_void_p] * 5 + [_i64] * 4 + [_f32, _int, _f32, _u64, _int, _c_void_p]),
+    "xfa_bwd_dropout": (_int, [_c_void_p] * 9 + [_i64] * 4 + [_f32, _int, _f32, _u64, _int, _c_void_p]),
     "xfa_status_string": (ctypes.c_char_p, [_int]),
 }
 
@@ -98,6 +100,10 @@ def _scale(scale, hd) -> float:
     return 1.0 / math.sqrt(hd) if scale is None else float(scale)
 
 
+def _seed(seed) -> int:
+    return int(seed) & 0xFFFFFFFFFFFFFFFF
+
+
 def _raise(st: int, where: str):
     if st != XFA_OK:
         raise XfaError(st, where)
@@ -142,23 +148,58 @@ def xfa_bwd(q, k, v, dout, lse, delta, dq, dk, dv, scale=None, causal=True, stre
     _raise(st, "xfa_bwd")
 
 
+def xfa_fwd_dropout(q, k, v, out, lse, scale=None, causal=True, dropout_p=0.0, seed=0, stream=None) -> None:
+    """xfa_fwd with dropout on the attention probabilities (keep decisions
+    from (seed, element index), kept weights scaled by 1/(1-p))."""
+    torch = _torch()
+    B, H, S, hd = q.shape
+    _check_same(q, q, k, v, out, shape=q.shape, dtype=q.dtype, names=("q", "k", "v", "out"))
+    _check_same(q, lse, shape=(B, H, S), dtype=torch.float32, names=("lse",))
+    st = lib().xfa_fwd_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                               B, H, S, hd, _scale(scale, hd), int(bool(causal)), float(dropout_p),
+                               _seed(seed), _dtype_code(q), _stream_handle(stream))
+    _raise(st, "xfa_fwd_dropout")
+
+
+def xfa_bwd_dropout(q, k, v, dout, lse, delta, dq, dk, dv, scale=None, causal=True, dropout_p=0.0, seed=0,
+                    stream=None) -> None:
+    """xfa_bwd of the forward that xfa_fwd_dropout ran with the same p and seed."""
+    torch = _torch()
+    B, H, S, hd = q.shape
+    _check_same(q, q, k, v, dout, dq, dk, dv, shape=q.shape, dtype=q.dtype,
+                names=("q", "k", "v", "dout", "dq", "dk", "dv"))
+    _check_same(q, lse, delta, shape=(B, H, S), dtype=torch.float32, names=("lse", "delta"))
+    st = lib().xfa_bwd_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+                               delta.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                               B, H, S, hd, _scale(scale, hd), int(bool(causal)), float(dropout_p),
+                               _seed(seed), _dtype_code(q), _stream_handle(stream))
+    _raise(st, "xfa_bwd_dropout")
+
+
 # ------------------------------------------------------------ conveniences
-def forward(q, k, v, scale=None, causal=True, stream=None):
-    """Allocate and return (out, lse)."""
+def forward(q, k, v, scale=None, causal=True, stream=None, dropout_p=0.0, seed=0):
+    """Allocate and return (out, lse).  dropout_p > 0 calls xfa_fwd_dropout."""
     torch = _torch()
     B, H, S, hd = q.shape
     out = torch.empty_like(q)
     lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
-    xfa_fwd(q, k, v, out, lse, scale, causal, stream)
+    if dropout_p:
+        xfa_fwd_dropout(q, k, v, out, lse, scale, causal, dropout_p, seed, stream)
+    else:
+        xfa_fwd(q, k, v, out, lse, scale, causal, stream)
     return out, lse
 
 
-def backward(q, k, v, out, dout, lse, scale=None, causal=True, stream=None):
-    """Run the preprocess and the backward; allocate and return (dq, dk, dv)."""
+def backward(q, k, v, out, dout, lse, scale=None, causal=True, stream=None, dropout_p=0.0, seed=0):
+    """Run the preprocess and the backward; allocate and return (dq, dk, dv).
+    dropout_p > 0 calls xfa_bwd_dropout (same p and seed as the forward)."""
     torch = _torch()
     B, H, S, hd = q.shape
     delta = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
     xfa_bwd_preprocess(out, dout, delta, scale, causal, stream)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    xfa_bwd(q, k, v, dout, lse, delta, dq, dk, dv, scale, causal, stream)
+    if dropout_p:
+        xfa_bwd_dropout(q, k, v, dout, lse, delta, dq, dk, dv, scale, causal, dropout_p, seed, stream)
+    else:
+        xfa_bwd(q, k, v, dout, lse, delta, dq, dk, dv, scale, causal, stream)
     return dq, dk, dv

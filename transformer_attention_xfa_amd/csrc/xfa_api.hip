@@ -48,6 +48,17 @@ xfa_status_t check_ptrs(std::initializer_list<const void*> ps) {
 
 xfa_status_t from_hip(hipError_t e) { return e == hipSuccess ? XFA_OK : XFA_ERR_HIP; }
 
+// Dropout probability p in [0, 1) -> the kernels' threshold and scale
+// (thresh = ceil(p 2^24): keep iff the generator's top 24 bits >= thresh,
+// the same decision as (bits / 2^24) >= p in float32; thresh 0 = off).
+xfa_status_t drop_args(float p, uint64_t seed, xfa::DropArgs* d) {
+  if (!(p >= 0.f && p < 1.f)) return XFA_ERR_INVALID_ARGUMENT;   // also rejects NaN
+  d->seed = seed;
+  d->thresh = (uint32_t)ceil((double)p * 16777216.0);
+  d->inv_keep = 1.f / (1.f - p);
+  return XFA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -60,6 +71,20 @@ xfa_status_t xfa_fwd(const void* q, const void* k, const void* v, void* out, flo
   if (st != XFA_OK || sh.empty) return st;
   if ((st = check_ptrs({q, k, v, out, lse})) != XFA_OK) return st;
   xfa::FwdArgs a{q, k, v, out, lse, sh.BH, sh.S, sh.hd, scale, causal, sh.bf16, (hipStream_t)stream};
+  return from_hip(xfa::launch_fwd(a));
+}
+
+xfa_status_t xfa_fwd_dropout(const void* q, const void* k, const void* v, void* out, float* lse,
+                             int64_t B, int64_t H, int64_t S, int64_t hd, float scale, int causal,
+                             float dropout_p, uint64_t seed, int dtype, void* stream) {
+  Shape sh;
+  xfa::DropArgs d;
+  xfa_status_t st = check_common(B, H, S, hd, scale, causal, dtype, &sh);
+  if (st == XFA_OK) st = drop_args(dropout_p, seed, &d);
+  if (st != XFA_OK || sh.empty) return st;
+  st = check_ptrs({q, k, v, out, lse});
+  if (st != XFA_OK) return st;
+  xfa::FwdArgs a{q, k, v, out, lse, sh.BH, sh.S, sh.hd, scale, causal, sh.bf16, (hipStream_t)stream, d};
   return from_hip(xfa::launch_fwd(a));
 }
 
@@ -84,6 +109,22 @@ xfa_status_t xfa_bwd(const void* q, const void* k, const void* v, const void* do
   if ((st = check_ptrs({q, k, v, dout, lse, delta, dq, dk, dv})) != XFA_OK) return st;
   xfa::BwdArgs a{q, k, v, dout, lse, delta, dq, dk, dv,
                  sh.BH, sh.S, sh.hd, scale, causal, sh.bf16, (hipStream_t)stream};
+  return from_hip(xfa::launch_bwd(a));
+}
+
+xfa_status_t xfa_bwd_dropout(const void* q, const void* k, const void* v, const void* dout,
+                             const float* lse, const float* delta, void* dq, void* dk, void* dv,
+                             int64_t B, int64_t H, int64_t S, int64_t hd, float scale, int causal,
+                             float dropout_p, uint64_t seed, int dtype, void* stream) {
+  Shape sh;
+  xfa::DropArgs d;
+  xfa_status_t st = check_common(B, H, S, hd, scale, causal, dtype, &sh);
+  if (st == XFA_OK) st = drop_args(dropout_p, seed, &d);
+  if (st != XFA_OK || sh.empty) return st;
+  st = check_ptrs({q, k, v, dout, lse, delta, dq, dk, dv});
+  if (st != XFA_OK) return st;
+  xfa::BwdArgs a{q, k, v, dout, lse, delta, dq, dk, dv,
+                 sh.BH, sh.S, sh.hd, scale, causal, sh.bf16, (hipStream_t)stream, d};
   return from_hip(xfa::launch_bwd(a));
 }
 

@@ -57,6 +57,7 @@ struct BwdParams {
   const float* Lse; const float* Dl;
   T* dQ; T* dK; T* dV;
   int S; float scale; float c_log2; int causal;
+  DropArgs drop;   // attention-probabilities dropout (used when DROP)
 };
 
 // ------------------------------------------------------------ key workgroups
@@ -76,7 +77,10 @@ struct KeyBuf {
   }
 };
 
-template <typename T, int HD, int NW>
+// DROP: the forward's dropout mask M (kept probabilities times 1 / (1 - p)),
+// regenerated from the seed and each element's index: dV takes P o M and
+// dS = P o (M o dP - D).
+template <typename T, int HD, int NW, bool DROP>
 __device__ __forceinline__ void key_role(const BwdParams<T>& p, int bh, int kt, char* smem) {
   using G = BlockGeo<T, HD, NW>;
   using M = typename G::M;
@@ -104,6 +108,21 @@ __device__ __forceinline__ void key_role(const BwdParams<T>& p, int bh, int kt, 
   constexpr int NBUF = KB::NBUF;
   auto buf = [&](int n) { return KB(smem + (size_t)((unsigned)n % NBUF) * KB::BYTES); };
   const TileRead<T, HD, NW> rd;
+
+  // dropout: element v of block n is query n NB + 8 (v / 4) + 4 h + v % 4 and
+  // this lane's key, flat index (bh S + query) S + kj; igold = index * kGolden
+  const uint64_t sg = (uint64_t)S * kGolden;
+  const uint64_t lane_g = ((uint64_t)bh * (uint64_t)S * (uint64_t)S + (uint64_t)kj) * kGolden;
+  auto block_g = [&](int n) { return lane_g + (uint64_t)(n * NB + 4 * h) * sg; };
+  // M of element v of the block with base bg (1 without dropout)
+  auto mask = [&](uint64_t bg, int v) {
+    if constexpr (DROP) {
+      const uint64_t ig = bg + (uint64_t)(8 * (v >> 2) + (v & 3)) * sg;
+      return drop_keep(p.drop.seed, ig, p.drop.thresh) ? p.drop.inv_keep : 0.f;
+    } else {
+      return 1.f;
+    }
+  };
 
   // this lane's key row of K and V: B operands of S = Q.K^T and dP = dO.V^T
   typename M::frag kf[NC], vf[NC];
@@ -152,6 +171,7 @@ __device__ __forceinline__ void key_role(const BwdParams<T>& p, int bh, int kt, 
   // (a block's L is read as -L log2 e, see prescale)
   auto finish = [&](auto masked, int n, f32x16 s, f32x16 dp) {
     KB b = buf(n);
+    const uint64_t bg = block_g(n);
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const f32x4 L4 = *reinterpret_cast<const f32x4*>(b.L + 8 * g + 4 * h);
@@ -160,8 +180,9 @@ __device__ __forceinline__ void key_role(const BwdParams<T>& p, int bh, int kt, 
       for (int e = 0; e < 4; ++e) {
         const int v = 4 * g + e;
         const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[v], p.c_log2, L4[e]));
-        s[v] = pr;
-        dp[v] = pr * (dp[v] - D4[e]);
+        const float m = mask(bg, v);
+        s[v] = pr * m;
+        dp[v] = pr * (dp[v] * m - D4[e]);
       }
     }
     if constexpr (decltype(masked)::value) {
@@ -247,6 +268,7 @@ __device__ __forceinline__ void key_role(const BwdParams<T>& p, int bh, int kt, 
       const f32x16& dp = pipe.cur(par).dp;
       f32x16 ps, ds;
       const int lo = kj - (n * NB + 4 * h);      // masked: query row rel sees key kj iff rel >= lo
+      const uint64_t bg = block_g(n);
       constexpr int NG = NU * NDB;               // gradient contraction pairs
       // LDS reads are spread over the contraction steps so that the matrix
       // core never waits behind a long queue of them: the score operands are
@@ -290,7 +312,8 @@ __device__ __forceinline__ void key_role(const BwdParams<T>& p, int bh, int kt, 
       auto ld_step = [&](int g) { return fin_step(4 * g) - 1; };
       auto softmax = [&](int v) {
         const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[v], p.c_log2, L4[v >> 2][v & 3]));
-        float pv = pr, dv = pr * (dp[v] - D4[v >> 2][v & 3]);
+        const float m = mask(bg, v);
+        float pv = pr * m, dv = pr * (dp[v] * m - D4[v >> 2][v & 3]);
         if constexpr (decltype(masked)::value) {
           const bool keep = 8 * (v >> 2) + (v & 3) >= lo;
           pv = keep ? pv : 0.f;
@@ -401,7 +424,8 @@ struct QueryBuf {
   }
 };
 
-template <typename T, int HD, int NW>
+// DROP: dS^T = P o (M o dP - D) with the forward's regenerated mask M.
+template <typename T, int HD, int NW, bool DROP>
 __device__ __forceinline__ void query_role(const BwdParams<T>& p, int bh, int qq, char* smem) {
   using G = BlockGeo<T, HD, NW>;
   using M = typename G::M;
@@ -447,6 +471,18 @@ __device__ __forceinline__ void query_role(const BwdParams<T>& p, int bh, int qq
   }
   float L2 = bload4(rL, (uint32_t)qi * 4u) * kLog2e;
   float Di = bload4(rD, (uint32_t)qi * 4u);
+  // dropout: element v of block n is key n NB + 8 (v / 4) + 4 h + v % 4 of
+  // this lane's query, flat index (bh S + qi) S + key; igold = index * kGolden
+  const uint64_t lane_g = ((uint64_t)bh * (uint64_t)S + (uint64_t)qi) * (uint64_t)S * kGolden;
+  auto block_g = [&](int n) { return lane_g + (uint64_t)(n * NB + 4 * h) * kGolden; };
+  auto mask = [&](uint64_t bg, int v) {
+    if constexpr (DROP) {
+      const uint64_t ig = bg + (uint64_t)(8 * (v >> 2) + (v & 3)) * kGolden;
+      return drop_keep(p.drop.seed, ig, p.drop.thresh) ? p.drop.inv_keep : 0.f;
+    } else {
+      return 1.f;
+    }
+  };
 
   f32x16 dqacc[NDB];
 #pragma unroll
@@ -478,10 +514,11 @@ __device__ __forceinline__ void query_role(const BwdParams<T>& p, int bh, int qq
   // dS^T = p (dp - D) with p = 2^(s c - L log2 e); dQ^T += K^T.dS^T
   auto finish = [&](auto masked, int n, f32x16 s, f32x16 dp) {
     QB b = buf(n);
+    const uint64_t bg = block_g(n);
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[v], p.c_log2, -L2));
-      dp[v] = pr * (dp[v] - Di);
+      dp[v] = pr * (dp[v] * mask(bg, v) - Di);
     }
     if constexpr (decltype(masked)::value) {
       // key j is seen by query qi iff j <= qi
@@ -536,6 +573,7 @@ __device__ __forceinline__ void query_role(const BwdParams<T>& p, int bh, int qq
       f32x16& dn = pipe.next(par).dp;
       f32x16 s = pipe.cur(par).s, dp = pipe.cur(par).dp;
       const int rel = qi - (n * NB + 4 * h);   // masked: key row r is seen iff r <= rel
+      const uint64_t bg = block_g(n);
       typename M::frag ka[NC], va[NC], ta[NG];
       auto read_sc = [&](int c) {
         ka[c] = rd.nat(bn.k, c);
@@ -557,7 +595,7 @@ __device__ __forceinline__ void query_role(const BwdParams<T>& p, int bh, int qq
 #pragma unroll
         for (int v = c * EPC; v < (c + 1) * EPC && v < 16; ++v) {
           const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[v], p.c_log2, -L2));
-          float ds = pr * (dp[v] - Di);
+          float ds = pr * (dp[v] * mask(bg, v) - Di);
           if constexpr (decltype(masked)::value) ds = (8 * (v >> 2) + (v & 3) > rel) ? 0.f : ds;
           dp[v] = ds;
         }
@@ -629,23 +667,25 @@ struct BwdCfg {
 // earliest keys see the most queries) need the whole register file, one wave
 // per SIMD; query workgroups (heaviest first: the last queries see the most
 // keys) fit two waves per SIMD for bf16.  A head's workgroups stay on one XCD.
-template <typename T, int HD>
+template <typename T, int HD, bool DROP>
 __global__ __launch_bounds__((BwdCfg<T, HD>::NW * 64), 1) void bwd_key_kernel(BwdParams<T> p, int nkt, int nwg) {
   using C = BwdCfg<T, HD>;
   __shared__ __attribute__((aligned(16))) char smem[C::KEY_BYTES];
   const int lid = xcd_logical(blockIdx.x, nwg);
   const int bh = lid / nkt;
-  key_role<T, HD, C::NW>(p, bh, lid - bh * nkt, smem);
+  key_role<T, HD, C::NW, DROP>(p, bh, lid - bh * nkt, smem);
 }
 
-template <typename T, int HD>
-__global__ __launch_bounds__((BwdCfg<T, HD>::NW * 64), (sizeof(T) == 2 ? 2 : 1)) void bwd_query_kernel(
+// (with dropout the generator's 64-bit arithmetic needs more than half the
+// register file: one workgroup per CU)
+template <typename T, int HD, bool DROP>
+__global__ __launch_bounds__((BwdCfg<T, HD>::NW * 64), (sizeof(T) == 2 && !DROP ? 2 : 1)) void bwd_query_kernel(
     BwdParams<T> p, int nqq, int nwg) {
   using C = BwdCfg<T, HD>;
   __shared__ __attribute__((aligned(16))) char smem[C::QUERY_BYTES];
   const int lid = xcd_logical(blockIdx.x, nwg);
   const int bh = lid / nqq;
-  query_role<T, HD, C::NW>(p, bh, nqq - 1 - (lid - bh * nqq), smem);
+  query_role<T, HD, C::NW, DROP>(p, bh, nqq - 1 - (lid - bh * nqq), smem);
 }
 
 template <typename T, int HD>
@@ -656,12 +696,18 @@ static hipError_t launch_bwd_t(const BwdArgs& a) {
   const int nkt = (int)((a.S + BKV - 1) / BKV);
   const int nqq = (int)((a.S + BQQ - 1) / BQQ);
   BwdParams<T> p{(const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.dout, a.lse, a.delta,
-                 (T*)a.dq, (T*)a.dk, (T*)a.dv, (int)a.S, a.scale, a.scale * kLog2e, a.causal};
+                 (T*)a.dq, (T*)a.dk, (T*)a.dv, (int)a.S, a.scale, a.scale * kLog2e, a.causal, a.drop};
   const int nk = (int)(a.BH * nkt), nq = (int)(a.BH * nqq);
-  hipLaunchKernelGGL((bwd_key_kernel<T, HD>), dim3(nk), dim3(C::NW * 64), 0, a.stream, p, nkt, nk);
+  if (a.drop.thresh)
+    hipLaunchKernelGGL((bwd_key_kernel<T, HD, true>), dim3(nk), dim3(C::NW * 64), 0, a.stream, p, nkt, nk);
+  else
+    hipLaunchKernelGGL((bwd_key_kernel<T, HD, false>), dim3(nk), dim3(C::NW * 64), 0, a.stream, p, nkt, nk);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_query_kernel<T, HD>), dim3(nq), dim3(C::NW * 64), 0, a.stream, p, nqq, nq);
+  if (a.drop.thresh)
+    hipLaunchKernelGGL((bwd_query_kernel<T, HD, true>), dim3(nq), dim3(C::NW * 64), 0, a.stream, p, nqq, nq);
+  else
+    hipLaunchKernelGGL((bwd_query_kernel<T, HD, false>), dim3(nq), dim3(C::NW * 64), 0, a.stream, p, nqq, nq);
   return hipGetLastError();
 }
 

@@ -38,6 +38,24 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+
+// Counter-based dropout generator (xtrain dropout design doc, "RNG: counter
+// based"): element i of the [B*H, S, S] attention probabilities is kept iff
+// the top 24 bits of splitmix64(seed XOR i * kGolden) reach thresh =
+// ceil(p 2^24), the same decision as u = (h >> 40) / 2^24 >= p in float32.
+// splitmix64 (Steele, Lea and Flood): one generator step from state z, i.e.
+// z + kGolden passed through two xorshift-multiply rounds and a xorshift.
+constexpr uint64_t kGolden = 0x9E3779B97F4A7C15ull;
+__device__ inline uint64_t splitmix64_step(uint64_t z) {
+  z += kGolden;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+// igold = i * kGolden (mod 2^64), formed incrementally by the callers
+__device__ inline bool drop_keep(uint64_t seed, uint64_t igold, uint32_t thresh) {
+  return (uint32_t)(splitmix64_step(seed ^ igold) >> 40) >= thresh;
+}
 constexpr float kNegInf = -__builtin_huge_valf();
 
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;

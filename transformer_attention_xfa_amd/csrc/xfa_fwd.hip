@@ -47,10 +47,13 @@ struct FwdBuf {
   }
 };
 
-template <typename T, int HD, int NW>
+// DROP: attention-probabilities dropout (keep bits regenerated from the seed
+// and the element index, never stored): the row sum l is taken over the
+// undropped weights, and P.V uses the kept weights times 1 / (1 - p).
+template <typename T, int HD, int NW, bool DROP>
 __global__ __launch_bounds__(NW * 64, (sizeof(T) == 2 ? 2 : 1)) void fwd_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, T* __restrict__ O,
-    float* __restrict__ Lse, int S, float c_log2, int causal, int nqt, int nwg) {
+    float* __restrict__ Lse, int S, float c_log2, int causal, int nqt, int nwg, DropArgs drop) {
   using G = BlockGeo<T, HD, NW>;
   using M = typename G::M;
   using FB = FwdBuf<T, HD, NW>;
@@ -142,10 +145,27 @@ __global__ __launch_bounds__(NW * 64, (sizeof(T) == 2 ? 2 : 1)) void fwd_kernel(
   // weight of element v and its contribution to the row sum (bf16: the
   // rounded weight that enters P.V)
   auto weight = [&](const f32x16& s, int v) { return __builtin_amdgcn_exp2f(__builtin_fmaf(s[v], c_log2, -m_ref)); };
+  // dropout: element v of block n is key n NB + 8 (v / 4) + 4 h + v % 4 of
+  // this lane's query, flat index (bh S + qi) S + key; igold = index * kGolden
+  const uint64_t lane_g = ((uint64_t)bh * (uint64_t)S + (uint64_t)qi) * (uint64_t)S * kGolden;
+  auto block_g = [&](int n) { return lane_g + (uint64_t)(n * NB + 4 * h) * kGolden; };
+  // weight of element v as it enters P.V; with dropout the row sum takes the
+  // undropped weight here (pfrag then skips it)
+  auto dropped = [&](float pv, uint64_t bg, int v) {
+    if constexpr (DROP) {
+      if constexpr (BF) l_run += (float)(bf16)pv;
+      else l_run += pv;
+      const uint64_t ig = bg + (uint64_t)(8 * (v >> 2) + (v & 3)) * kGolden;
+      pv = drop_keep(drop.seed, ig, drop.thresh) ? pv * drop.inv_keep : 0.f;
+    }
+    return pv;
+  };
   // P^T fragment u of block n's weights; the row sum over the values it holds
   auto pfrag = [&](const f32x16& p, int u) {
     const typename M::frag pf = frag_from_acc(p, u, T{});
-    if constexpr (BF) {
+    if constexpr (DROP) {
+      // the row sum was taken in dropped()
+    } else if constexpr (BF) {
       typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
       const bf16x2 one2{(bf16)1.f, (bf16)1.f};
 #pragma unroll
@@ -161,8 +181,9 @@ __global__ __launch_bounds__(NW * 64, (sizeof(T) == 2 ? 2 : 1)) void fwd_kernel(
   auto finish = [&](auto masked, int n, f32x16 s, const f32x16&) {
     FB b = buf(n);
     prepare(masked, n, s);
+    const uint64_t bg = block_g(n);
 #pragma unroll
-    for (int v = 0; v < 16; ++v) s[v] = weight(s, v);
+    for (int v = 0; v < 16; ++v) s[v] = dropped(weight(s, v), bg, v);
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
       const typename M::frag pf = pfrag(s, u);
@@ -195,6 +216,7 @@ __global__ __launch_bounds__(NW * 64, (sizeof(T) == 2 ? 2 : 1)) void fwd_kernel(
       for (int c = 0; c < PD && c < NC; ++c) read_k(c);
       fetch(n + NBUF - 1);         // into the buffer of block n-1, finished before the last barrier
       prepare(masked, n, s);
+      const uint64_t bg = block_g(n);
       sn = zero16();
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
@@ -207,7 +229,7 @@ __global__ __launch_bounds__(NW * 64, (sizeof(T) == 2 ? 2 : 1)) void fwd_kernel(
         for (int v = c * EPC; v < (c + 1) * EPC && v < 16; ++v) {
           // pinned here: otherwise the compiler sinks the arithmetic to the
           // fragment conversion, where no contraction overlaps it
-          float pv = weight(s, v);
+          float pv = dropped(weight(s, v), bg, v);
           settle(pv);
           s[v] = pv;
         }
@@ -278,9 +300,14 @@ static hipError_t launch_fwd_t(const FwdArgs& a) {
   constexpr int BQ = NW * 32;
   const int nqt = (int)((a.S + BQ - 1) / BQ);
   const int nwg = (int)(a.BH * nqt);
-  hipLaunchKernelGGL((fwd_kernel<T, HD, NW>), dim3(nwg), dim3(NW * 64), 0, a.stream,
-                     (const T*)a.q, (const T*)a.k, (const T*)a.v, (T*)a.out, a.lse, (int)a.S,
-                     a.scale * kLog2e, a.causal, nqt, nwg);
+  if (a.drop.thresh)
+    hipLaunchKernelGGL((fwd_kernel<T, HD, NW, true>), dim3(nwg), dim3(NW * 64), 0, a.stream,
+                       (const T*)a.q, (const T*)a.k, (const T*)a.v, (T*)a.out, a.lse, (int)a.S,
+                       a.scale * kLog2e, a.causal, nqt, nwg, a.drop);
+  else
+    hipLaunchKernelGGL((fwd_kernel<T, HD, NW, false>), dim3(nwg), dim3(NW * 64), 0, a.stream,
+                       (const T*)a.q, (const T*)a.k, (const T*)a.v, (T*)a.out, a.lse, (int)a.S,
+                       a.scale * kLog2e, a.causal, nqt, nwg, a.drop);
   return hipGetLastError();
 }
 
