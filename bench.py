@@ -49,7 +49,7 @@ KERNEL_NAME = {"fwd": "fwd_kernel", "pre": "bwd_pre_kernel", "bwd": "bwd_key_ker
 def source_digest(phase: str) -> str:
     h = hashlib.sha256()
     for rel in (KERNEL_SRC[phase], "transformer_attention_xfa_amd/csrc/xfa_common.h",
-                "transformer_attention_xfa_amd/csrc/xfa_stage.h"):
+                "transformer_attention_xfa_amd/csrc/xfa_stage.h", "transformer_attention_xfa_amd/build.py"):
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]

@@ -722,8 +722,17 @@ static hipError_t bwd_dispatch(const BwdArgs& a) {
   return hipErrorInvalidValue;
 }
 
+// This file is compiled with matrix-core results in VGPRs (the build's
+// per-file flags) and instantiates the bf16 kernels; xfa_bwd_f32.hip includes
+// it with XFA_BWD_F32 defined and instantiates the fp32 kernels without that
+// option (the fp32 hd 128 key kernel with dropout would spill under it).
+#ifndef XFA_BWD_F32
+hipError_t launch_bwd_f32(const BwdArgs& a);
 hipError_t launch_bwd(const BwdArgs& a) {
-  return a.bf16 ? bwd_dispatch<bf16>(a) : bwd_dispatch<float>(a);
+  return a.bf16 ? bwd_dispatch<bf16>(a) : launch_bwd_f32(a);
 }
+#else
+hipError_t launch_bwd_f32(const BwdArgs& a) { return bwd_dispatch<float>(a); }
+#endif
 
 }  // namespace xfa

@@ -46,15 +46,18 @@ constexpr float kLn2 = 0.6931471805599453f;
 // splitmix64 (Steele, Lea and Flood): one generator step from state z, i.e.
 // z + kGolden passed through two xorshift-multiply rounds and a xorshift.
 constexpr uint64_t kGolden = 0x9E3779B97F4A7C15ull;
-__device__ inline uint64_t splitmix64_step(uint64_t z) {
-  z += kGolden;
-  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
-  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
-  return z ^ (z >> 31);
-}
-// igold = i * kGolden (mod 2^64), formed incrementally by the callers
+// igold = i * kGolden (mod 2^64), formed incrementally by the callers.
+// Only bits 40..63 of the hash decide, and the final xorshift by 31 leaves
+// them as they are, so the last product is formed for its top 32 bits only
+// (its low-half carry included; the multiplier 0x94D049BB133111EB taken in
+// 32-bit halves) and compared with thresh << 8.
 __device__ inline bool drop_keep(uint64_t seed, uint64_t igold, uint32_t thresh) {
-  return (uint32_t)(splitmix64_step(seed ^ igold) >> 40) >= thresh;
+  uint64_t z = (seed ^ igold) + kGolden;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z ^= z >> 27;
+  const uint32_t lo = (uint32_t)z, hi = (uint32_t)(z >> 32);
+  const uint32_t top = __umulhi(lo, 0x133111EBu) + lo * 0x94D049BBu + hi * 0x133111EBu;
+  return top >= (thresh << 8);
 }
 constexpr float kNegInf = -__builtin_huge_valf();
 
