@@ -142,6 +142,15 @@ __global__ __launch_bounds__(NW * 64, (sizeof(T) == 2 ? 2 : 1)) void fwd_kernel(
       for (int d = 0; d < NDB; ++d) oacc[d] *= alpha;
     }
   };
+  // the mask alone (idempotent); the pipelined bf16 body leaves the block
+  // maximum out and checks the weights instead (see below)
+  auto mask_only = [&](auto masked, int n, f32x16& s) {
+    if constexpr (decltype(masked)::value) {
+      const int rel = key_lim - (n * NB + 4 * h);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) s[v] = (8 * (v >> 2) + (v & 3) > rel) ? kNegInf : s[v];
+    }
+  };
   // weight of element v and its contribution to the row sum (bf16: the
   // rounded weight that enters P.V)
   auto weight = [&](const f32x16& s, int v) { return __builtin_amdgcn_exp2f(__builtin_fmaf(s[v], c_log2, -m_ref)); };
@@ -176,6 +185,25 @@ __global__ __launch_bounds__(NW * 64, (sizeof(T) == 2 ? 2 : 1)) void fwd_kernel(
     }
     return pf;
   };
+  // bf16 P^T fragments of a block's weights and this lane's sum of them
+  constexpr float kSumMax = 128.f;   // 2^7: a block sum this small bounds every weight by it
+  auto block_sum = [&](const f32x16& p, typename M::frag (&pf)[NU]) {
+    float lb = 0.f;
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      pf[u] = frag_from_acc(p, u, T{});
+      if constexpr (BF) {
+        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+        const bf16x2 one2{(bf16)1.f, (bf16)1.f};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          lb = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[u][2 * e], pf[u][2 * e + 1]}, one2, lb, false);
+      } else {
+        lb += pf[u];
+      }
+    }
+    return lb;
+  };
   // the whole of block n: weights, row sum and O^T += V^T . P^T (the fourth
   // argument, the pipeline's second tile, is unused here)
   auto finish = [&](auto masked, int n, f32x16 s, const f32x16&) {
@@ -204,6 +232,9 @@ __global__ __launch_bounds__(NW * 64, (sizeof(T) == 2 ? 2 : 1)) void fwd_kernel(
     __syncthreads();
     f32x16 sa, sb, pa, pb;          // score tiles of blocks n and n+1 (pa, pb unused)
     sblock(0, sa);
+    // block 0 sets the reference maximum (m_ref starts at -inf)
+    if (0 >= nm) prepare(std::true_type{}, 0, sa);
+    else prepare(std::false_type{}, 0, sa);
     Pipe pipe(sa, pa, sb, pb);
     auto body = [&](auto masked, auto par, int n) {
       FB bn = buf(n + 1), bc = buf(n);
@@ -215,7 +246,8 @@ __global__ __launch_bounds__(NW * 64, (sizeof(T) == 2 ? 2 : 1)) void fwd_kernel(
 #pragma unroll
       for (int c = 0; c < PD && c < NC; ++c) read_k(c);
       fetch(n + NBUF - 1);         // into the buffer of block n-1, finished before the last barrier
-      prepare(masked, n, s);
+      if constexpr (DROP) prepare(masked, n, s);
+      else mask_only(masked, n, s);
       const uint64_t bg = block_g(n);
       sn = zero16();
 #pragma unroll
@@ -235,8 +267,27 @@ __global__ __launch_bounds__(NW * 64, (sizeof(T) == 2 ? 2 : 1)) void fwd_kernel(
         }
       }
       __builtin_amdgcn_sched_barrier(0);
+      if constexpr (DROP) {
 #pragma unroll
-      for (int u = 0; u < NU; ++u) pf[u] = pfrag(s, u);
+        for (int u = 0; u < NU; ++u) pf[u] = pfrag(s, u);
+      } else {
+        // The weights were formed against the reference maximum without
+        // the block maximum.  While each lane's block sum stays at most
+        // 2^kRescale every weight does too, which is all the reference has
+        // to guarantee; otherwise (the first blocks of a row, a jump of the
+        // logits, an overflow) the block is redone the full way: its scores
+        // again from the K tile still in LDS, mask, maximum and rescale,
+        // weights.  m_ref moves exactly as with the maximum taken first.
+        float lb = block_sum(s, pf);
+        if (__builtin_amdgcn_ballot_w64(!(lb <= kSumMax))) {
+          sblock(n, s);
+          prepare(masked, n, s);
+#pragma unroll
+          for (int v = 0; v < 16; ++v) s[v] = weight(s, v);
+          lb = block_sum(s, pf);
+        }
+        l_run += lb;
+      }
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
         __builtin_amdgcn_sched_barrier(0);
