@@ -115,6 +115,10 @@ def test_size_limits():
         assert _pre(S=1 << 22, hd=128, dtype=dtype) == UNSUP
         assert _bwd(S=1 << 22, hd=128, dtype=dtype) == UNSUP
         assert _bwd(S=1 << 23, hd=64, dtype=dtype) == UNSUP
+        # the staging past the end counts too: S*hd*4 < 2^31 but (S+256)*hd*4 is not
+        assert _fwd(S=(1 << 22) - 200, hd=128, dtype=dtype) == UNSUP
+        assert _fwd_drop(S=(1 << 22) - 200, hd=128, dtype=dtype) == UNSUP
+        assert _bwd(S=(1 << 22) - 200, hd=128, dtype=dtype) == UNSUP
 
 
 @pytest.mark.parametrize("call", [_fwd_drop, _bwd_drop])

@@ -27,8 +27,10 @@ xfa_status_t check_common(int64_t B, int64_t H, int64_t S, int64_t hd, float sca
   // the kernels index positions with int and launch one workgroup per
   // (head, 32..128-row tile) on a 1-D grid
   if (S > (int64_t(1) << 30)) return XFA_ERR_UNSUPPORTED;
-  // one head of one fp32 tensor must fit a 32-bit byte range
-  if (S * hd * 4 > int64_t(INT32_MAX)) return XFA_ERR_UNSUPPORTED;
+  // one head of one fp32 tensor, plus the blocks the kernels stage past its
+  // end (fewer than 256 rows), must stay below 2^31 bytes: the staging
+  // offsets of out-of-range lanes start at 2^31 and must not wrap
+  if ((S + 256) * hd * 4 > int64_t(INT32_MAX)) return XFA_ERR_UNSUPPORTED;
   if (B > 0 && H > INT64_MAX / B) return XFA_ERR_UNSUPPORTED;
   const int64_t BH = B * H;
   if (BH > 0 && (S + 31) / 32 > int64_t(INT32_MAX) / BH) return XFA_ERR_UNSUPPORTED;

@@ -239,8 +239,9 @@ struct Dma {
   __device__ inline void issue(uint32_t base, int row0) const {
 #pragma unroll
     for (int t = 0; t < NPW; ++t) {
-      // an out-of-range slot stays out of range whatever the row offset
-      const uint32_t off = (rel[t] + (uint32_t)row0 * step[t]) | (rel[t] & 0x80000000u);
+      // an out-of-range slot (rel = 2^31) stays at or above 2^31 without
+      // wrapping: the entry points keep (S + 256) rows of fp32 below 2^31 bytes
+      const uint32_t off = rel[t] + (uint32_t)row0 * step[t];
       dma16(desc[t], off, base + dst[t]);
     }
   }
