@@ -3,17 +3,17 @@ fused op (T14 flash-attention design doc: the composed path the fused kernel
 replaces, and its measured-results section, which compares the two on
 throughput and peak memory).
 
-Composed attention materialises the scores: S = Q K^T * scale by a batched
-GEMM, the causal mask and a softmax writing the [B, H, S, S] probabilities P,
-out = P V by a second GEMM; the backward keeps P and forms dV, dP, dS, dQ, dK
-with three more GEMMs and elementwise work on S x S tensors.  The GEMMs and
-the softmax are library kernels (torch on ROCm: hipBLASLt and its softmax);
-this is a comparator, not a second implementation of the op, and it computes
-all S*S products where the fused op skips the masked half.  Every batched
-product is given contiguous operands (the transposes are formed as small
-[.., hd, S] copies), and the softmax runs in fp32.
+Composed attention materialises the scores: S = Q K^T by a batched library
+GEMM (hipBLASLt through torch), then a causal row softmax written as a HIP
+kernel of its own (comparator_kernels/causal_softmax.hip: scale, mask and
+softmax in one pass over the scores, writing the [B, H, S, S] probabilities
+P in the inputs' dtype), then out = P V by a second GEMM; the backward keeps
+P and forms dV, dP, dS, dQ, dK with three more GEMMs and elementwise work on
+S x S tensors.  This is a comparator, not a second implementation of the op:
+it computes all S*S products where the fused op skips the masked half.
+Every batched product is given contiguous operands (the transposes are
+formed as small [.., hd, S] copies).
 """
-
 from __future__ import annotations
 
 import time
@@ -21,17 +21,49 @@ import time
 import numpy as np
 
 
+_softmax_lib = None
+
+
+def _softmax():
+    """xfa_comparator_causal_softmax from comparator_kernels/libcomposed.so."""
+    global _softmax_lib
+    if _softmax_lib is None:
+        import ctypes
+        import os
+
+        path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "comparator_kernels", "libcomposed.so")
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} not built; run `python -c 'import __graft_entry__ as g; g.build()'`")
+        lib = ctypes.CDLL(path)
+        fn = lib.xfa_comparator_causal_softmax
+        fn.restype = ctypes.c_int
+        fn.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_float,
+                       ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+        _softmax_lib = fn
+    return _softmax_lib
+
+
+def causal_softmax(s, scale, causal):
+    """P = softmax(mask(s * scale)) row by row for contiguous [..., S, S]
+    scores (bf16 or fp32) on the GPU, by the comparator's HIP kernel."""
+    import torch
+
+    S = s.shape[-1]
+    assert s.is_contiguous() and s.shape[-2] == S and s.dtype in (torch.bfloat16, torch.float32)
+    p = torch.empty_like(s)
+    st = _softmax()(s.data_ptr(), p.data_ptr(), s.numel() // (S * S), S, float(scale), int(bool(causal)),
+                    1 if s.dtype == torch.bfloat16 else 0, torch.cuda.current_stream().cuda_stream)
+    if st != 0:
+        raise RuntimeError(f"xfa_comparator_causal_softmax failed (status {st})")
+    return p
+
+
 def composed_forward(q, k, v, scale, causal):
     """out, P for [B, H, S, hd] q, k, v (P kept for the backward)."""
     import torch
 
     s = torch.matmul(q, k.transpose(-1, -2).contiguous())
-    s = s.float() * scale
-    if causal:
-        S = q.shape[-2]
-        mask = torch.ones(S, S, dtype=torch.bool, device=q.device).triu(1)
-        s.masked_fill_(mask, float("-inf"))
-    p = torch.softmax(s, dim=-1).to(q.dtype)
+    p = causal_softmax(s, scale, causal)
     del s
     return torch.matmul(p, v), p
 
@@ -116,7 +148,8 @@ def comparator_record(x, steps, warmup, fused_ms_step):
     flop = w.fwd_flop + w.bwd_flop
     ms = r["fwd_ms"] + r["bwd_ms"]
     return {
-        "kind": "composed attention (library GEMMs and softmax, [B,H,S,S] probabilities kept for the backward)",
+        "kind": "composed attention (library GEMMs, HIP causal-softmax kernel, [B,H,S,S] probabilities kept "
+                "for the backward)",
         "fwd_ms": round(r["fwd_ms"], 3), "bwd_ms": round(r["bwd_ms"], 3), "ms_per_step": round(ms, 3),
         "value": round(flop / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
         "note": "same algorithmic flop count as the fused op; the composed path computes all S*S products",

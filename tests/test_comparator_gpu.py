@@ -44,3 +44,28 @@ def test_composed_matches_oracle_and_fused(dtype, S, hd, causal):
             ef = np.abs(f[0, bh].float().cpu().numpy() - r).max() / den
             say(f"  head {bh} {name}: composed {ec:.3g} fused {ef:.3g}")
             assert ec <= tol and ef <= tol, (name, ec, ef)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("S,causal", [(256, True), (300, True), (200, False), (1, True)])
+def test_causal_softmax_kernel(dtype, S, causal):
+    # the comparator's softmax step against float64 NumPy on the same scores
+    # (S = 300 and 200 take the kernel's unaligned per-element path)
+    rng = np.random.default_rng(S)
+    x = (rng.standard_normal((1, 2, S, S)) * 3).astype(np.float32)
+    t = torch.from_numpy(x).cuda()
+    if dtype == "bf16":
+        t = t.to(torch.bfloat16)
+    xs = t.float().cpu().numpy().astype(np.float64) * 0.125
+    if causal:
+        xs = np.where(np.arange(S)[None, :] > np.arange(S)[:, None], -np.inf, xs)
+    ref = np.exp(xs - xs.max(-1, keepdims=True))
+    ref /= ref.sum(-1, keepdims=True)
+    p = comparator.causal_softmax(t, 0.125, causal)
+    torch.cuda.synchronize()
+    got = p.float().cpu().numpy()
+    err = np.abs(got - ref).max()
+    say(f"causal_softmax {dtype} S={S} causal={causal}: max err {err:.3g}")
+    assert err <= (4e-3 if dtype == "bf16" else 1e-6)
+    if causal:
+        assert np.all(got[..., np.triu_indices(S, 1)[0], np.triu_indices(S, 1)[1]] == 0)

@@ -5,6 +5,9 @@
 Each ``csrc/*.hip`` file is compiled to an object under ``_build/`` at the
 repository root and the objects are linked into
 ``transformer_attention_xfa_amd/libxfa.so``.  It always recompiles.
+``build_comparator()`` compiles the benchmark comparator's softmax kernel
+(``comparator_kernels/``) into ``comparator_kernels/libcomposed.so``, a
+library of its own: it is not part of the attention path.
 """
 
 from __future__ import annotations
@@ -84,5 +87,23 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+COMPARATOR_DIR = os.path.join(ROOT, "comparator_kernels")
+COMPARATOR_LIB = os.path.join(COMPARATOR_DIR, "libcomposed.so")
+
+
+def build_comparator(verbose: bool = False) -> str:
+    srcs = sorted(glob.glob(os.path.join(COMPARATOR_DIR, "*.hip")))
+    tmp = COMPARATOR_LIB + ".tmp"
+    cmd = [hipcc(), *FLAGS, "-shared", "-o", tmp, *srcs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on the comparator kernels:\n{' '.join(cmd)}\n{r.stdout}{r.stderr}")
+    os.replace(tmp, COMPARATOR_LIB)
+    if verbose:
+        print("built", COMPARATOR_LIB, file=sys.stderr)
+    return COMPARATOR_LIB
+
+
 if __name__ == "__main__":
     build(verbose=True)
+    build_comparator(verbose=True)
