@@ -1,7 +1,7 @@
 """Throughput of the fused causal attention path on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--comparator]
-                    [--dropout P]
+                    [--dropout P] [--graph]
 
 One step is one pass of the whole path over one batch: xfa_fwd, then
 xfa_bwd_preprocess, then xfa_bwd, with inputs resident in HBM.  The default
@@ -14,7 +14,9 @@ on a bounded sample of the same workload.  --comparator adds composed
 attention (comparator.py) on the same inputs: its time and both paths' peak
 memory.  --dropout P adds the same step with dropout on the attention
 probabilities (xfa_fwd_dropout / xfa_bwd_dropout) and its cost over the plain
-step; the headline value is always the plain step.
+step; the headline value is always the plain step.  --graph adds the step
+captured once in a HIP graph and replayed (the same kernels, without the
+per-launch host overhead that dominates the small workloads).
 """
 
 from __future__ import annotations
@@ -128,6 +130,49 @@ def gpu_bench(x, steps: int, warmup: int, dropout_p: float = 0.0, seed: int = 0x
         {p: float(np.median(v)) for p, v in ms.items()}, name
 
 
+def graph_bench(x, steps: int, warmup: int):
+    """ms per step of the plain step captured in one HIP graph and replayed."""
+    import torch
+
+    import transformer_attention_xfa_amd as xfa
+
+    w = x.w
+    dev = torch.device("cuda", 0)
+    if w.dtype == "bf16":
+        q, k, v, do = (torch.from_numpy(getattr(x, n + "_bits").view(np.int16)).view(torch.bfloat16).to(dev)
+                       for n in ("q", "k", "v", "do"))
+    else:
+        q, k, v, do = (torch.from_numpy(getattr(x, n)).to(dev) for n in ("q", "k", "v", "do"))
+    B, H, S, hd = w.shape
+    out = torch.empty_like(q)
+    lse = torch.empty((B, H, S), dtype=torch.float32, device=dev)
+    delta = torch.empty_like(lse)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+
+    def step():
+        xfa.xfa_fwd(q, k, v, out, lse, w.sm_scale, w.causal)
+        xfa.xfa_bwd_preprocess(out, do, delta, w.sm_scale, w.causal)
+        xfa.xfa_bwd(q, k, v, do, lse, delta, dq, dk, dv, w.sm_scale, w.causal)
+
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        step()
+    torch.cuda.current_stream().wait_stream(cap)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cap):
+        step()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        g.replay()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
+
+
 def cpu_baseline(x, n_heads: int):
     """The oracle, untuned, on the first n_heads heads of the workload (fwd + bwd)."""
     from oracle import attention_backward_head, attention_forward_head
@@ -169,6 +214,8 @@ def main(argv=None):
     ap.add_argument("--cpu-heads", type=int, default=32)
     ap.add_argument("--comparator", action="store_true",
                     help="also time composed attention (library GEMMs + softmax) and both paths' peak memory")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the plain step captured in a HIP graph and replayed")
     ap.add_argument("--dropout", type=float, default=0.0, metavar="P",
                     help="also time the step with dropout probability P on the attention probabilities")
     args = ap.parse_args(argv)
@@ -230,6 +277,10 @@ def main(argv=None):
         "phases": phases,
         "device": device,
     }
+    if args.graph:
+        g_ms = graph_bench(x, args.steps, args.warmup)
+        rec["graph"] = {"ms_per_step": round(g_ms, 4), "value": round(flop / (g_ms * 1e-3) / 1e12, 2),
+                        "unit": "TFLOP/s", "note": "the same step captured once in a HIP graph and replayed"}
     if args.dropout:
         d_step, d_mean, _, _ = gpu_bench(x, args.steps, args.warmup, dropout_p=args.dropout)
         rec["dropout"] = {
