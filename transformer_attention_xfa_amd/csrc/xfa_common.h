@@ -123,9 +123,6 @@ __device__ inline bf16x8 frag_from_acc(const f32x16& c, int u, bf16) {
 }
 __device__ inline float frag_from_acc(const f32x16& c, int u, float) { return c[u]; }
 
-// Row of C-tile element v for lane half h.
-__device__ inline int acc_row(int v, int h) { return 8 * (v >> 2) + 4 * h + (v & 3); }
-
 // Value of the same element in the other lane half (lane l ^ 32).
 __device__ inline float swap_halves(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -143,10 +140,6 @@ template <> struct Vec16<float> { typedef f32x4 type; static constexpr int N = 4
 template <typename T>
 __device__ inline typename Vec16<T>::type ld16(const T* p) {
   return *reinterpret_cast<const typename Vec16<T>::type*>(p);
-}
-template <typename T>
-__device__ inline void st16(T* p, const typename Vec16<T>::type& v) {
-  *reinterpret_cast<typename Vec16<T>::type*>(p) = v;
 }
 
 // ------------------------------------------------ buffer-resource access
@@ -174,9 +167,6 @@ __device__ inline void bstore8(rsrc_t r, uint32_t off, u32x2 v) { __builtin_amdg
 __device__ inline void bstore4(rsrc_t r, uint32_t off, float v) {
   __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);
 }
-__device__ inline void batomic_add(rsrc_t r, uint32_t off, float v) {
-  __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(v, r, off, 0, 0);
-}
 
 // Four consecutive results of a C tile as an 8-byte (bf16) or 16-byte (fp32) store.
 __device__ inline void bstore_row4(rsrc_t r, uint32_t off, float a, float b, float c, float d, bf16) {
@@ -185,43 +175,6 @@ __device__ inline void bstore_row4(rsrc_t r, uint32_t off, float a, float b, flo
 }
 __device__ inline void bstore_row4(rsrc_t r, uint32_t off, float a, float b, float c, float d, float) {
   bstore16(r, off, u32x4{__float_as_uint(a), __float_as_uint(b), __float_as_uint(c), __float_as_uint(d)});
-}
-
-// ------------------------------------------------ transposed bf16 tiles
-// Operands whose contraction index runs along the rows of a row-major tile
-// (V for P.V, Q and dO for the dK / dV sums, K for dQ) are kept in LDS
-// transposed: T[c][pos] holds X[row][c] for the tile's R rows, so that an
-// operand fragment (8 k-values of one column) is a single 16-byte read.  The
-// fragment a result-order operand needs (rows 8a + 4h + b of a 16-row group
-// for slot 4a + b of lane half h) becomes contiguous by storing row r at
-// position swap23(r) (bits 2 and 3 of r exchanged).  Each T row holds R/8
-// 16-byte chunks; chunks are XOR-swizzled by the row index so that 16
-// consecutive T rows read at the same logical chunk hit distinct banks.
-//
-// Staging: a unit is a 4-row x 2-column block loaded with four 4-byte loads
-// (rows r..r+3, columns c, c+1); two byte permutes make the 4-row groups of
-// column c and column c+1, each written as 8 bytes.  Lanes whose index has
-// bit 3 set write column c+1 first, which spreads each write across both
-// halves of the banks.
-template <int R>
-struct TTile {
-  static constexpr int NCH = R / 8;                       // 16-byte chunks per T row
-  static constexpr int RPB = R >= 128 ? 1 : 128 / R;      // T rows per 256-byte bank sweep
-  static constexpr int ROWW = R / 2;                      // dwords per T row
-  __device__ static inline int sw(int c) { return (c / RPB) & (NCH - 1); }
-  // dword address of the chunk holding positions 8j..8j+7 of T row c
-  __device__ static inline int chunk_dw(int c, int j) { return c * ROWW + 4 * (j ^ sw(c)); }
-};
-
-__device__ inline int swap23(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
-
-// Four rows x two bf16 columns (as loaded) -> the 4-row groups of each column.
-__device__ inline void transpose_4x2(const unsigned x[4], u32x2& col0, u32x2& col1) {
-  // v_perm_b32(a, b, sel): byte k of the result is byte sel[k] of {a (bytes 4..7), b (bytes 0..3)}
-  col0[0] = __builtin_amdgcn_perm(x[1], x[0], 0x05040100u);   // r0.c0, r1.c0
-  col0[1] = __builtin_amdgcn_perm(x[3], x[2], 0x05040100u);   // r2.c0, r3.c0
-  col1[0] = __builtin_amdgcn_perm(x[1], x[0], 0x07060302u);   // r0.c1, r1.c1
-  col1[1] = __builtin_amdgcn_perm(x[3], x[2], 0x07060302u);   // r2.c1, r3.c1
 }
 
 // Workgroup order for 8 XCDs: the hardware hands consecutive workgroup ids to

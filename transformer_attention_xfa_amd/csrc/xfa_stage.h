@@ -29,7 +29,6 @@ struct BlockGeo {
   using M = Mma<T>;
   static constexpr bool BF = sizeof(T) == 2;
   static constexpr int NB = 32;
-  static constexpr int NT = NW * 64;
   static constexpr int HDP = HD < 32 ? 32 : HD;
   static constexpr int NDB = HDP / 32;           // 32-row d blocks
   static constexpr int NC = HD / M::KD;          // instructions along d
