@@ -259,3 +259,21 @@ def test_empty_and_error_paths():
     q = torch.zeros((1, 1, 8, 64), dtype=torch.float16, device="cuda")
     with pytest.raises(TypeError):
         xfa.forward(q, q, q)
+
+
+# ------------------------------------------------ other kernels at scale
+@pytest.mark.parametrize("dtype,B,H,S,hd,causal", [
+    ("bf16", 2, 4, 4096, 128, False),     # non-causal at the C4 length
+    ("bf16", 1, 4, 2048, 32, True),       # small head dim over many blocks
+    ("bf16", 1, 4, 2047, 16, False),      # ragged end, smallest head dim
+    ("f32", 1, 2, 1024, 128, True),       # fp32 kernels at hd 128 over many blocks
+    ("f32", 1, 2, 1000, 64, False),
+])
+def test_other_shapes_at_scale(dtype, B, H, S, hd, causal):
+    w = workloads.Workload(f"scale_{dtype}_s{S}_hd{hd}_{'c' if causal else 'f'}", dtype, B, H, S, hd,
+                           seed=3000 + S + hd, causal=causal, do_std=1.0 if dtype == "f32" else 0.1)
+    x = workloads.make_inputs(w)
+    g = run_gpu(x)
+    for bh in (0, w.BH - 1):
+        compare_head(x, g, bh, row_block=1024)
+    check_invariants(x, g)
