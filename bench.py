@@ -126,8 +126,10 @@ def gpu_bench(x, steps: int, warmup: int, dropout_p: float = 0.0, seed: int = 0x
         ms["bwd"].append(ev[2].elapsed_time(ev[3]))
     assert torch.isfinite(out).all() and torch.isfinite(dq).all(), "non-finite output"
     name = torch.cuda.get_device_name(dev)
-    return (t1 - t0) * 1e3 / steps, {p: float(np.mean(v)) for p, v in ms.items()}, \
-        {p: float(np.median(v)) for p, v in ms.items()}, name
+    stats = {"mean": {p: float(np.mean(v)) for p, v in ms.items()},
+             "median": {p: float(np.median(v)) for p, v in ms.items()},
+             "min": {p: float(np.min(v)) for p, v in ms.items()}}
+    return (t1 - t0) * 1e3 / steps, stats, name
 
 
 def graph_bench(x, steps: int, warmup: int):
@@ -173,6 +175,17 @@ def graph_bench(x, steps: int, warmup: int):
     return (time.perf_counter() - t0) * 1e3 / steps
 
 
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
 def cpu_baseline(x, n_heads: int):
     """The oracle, untuned, on the first n_heads heads of the workload (fwd + bwd)."""
     from oracle import attention_backward_head, attention_forward_head
@@ -186,12 +199,17 @@ def cpu_baseline(x, n_heads: int):
     except Exception:
         pass
     heads = [[x.f64(n, h) for n in ("q", "k", "v", "do")] for h in range(n_heads)]
-    t0 = time.perf_counter()
+    t_fwd = t_bwd = 0.0
     for q, k, v, do in heads:
+        t0 = time.perf_counter()
         attention_forward_head(q, k, v, w.sm_scale, w.causal, row_block=1024)
+        t1 = time.perf_counter()
         attention_backward_head(q, k, v, do, w.sm_scale, w.causal, row_block=1024)
-    dt = time.perf_counter() - t0
-    flop = (w.fwd_flop + w.bwd_flop) / w.BH * n_heads
+        t_fwd += t1 - t0
+        t_bwd += time.perf_counter() - t1
+    dt = t_fwd + t_bwd
+    frac = n_heads / w.BH
+    flop = (w.fwd_flop + w.bwd_flop) * frac
     return {
         "value": round(flop / dt / 1e12, 6),
         "unit": "TFLOP/s",
@@ -199,8 +217,12 @@ def cpu_baseline(x, n_heads: int):
         "kind": "oracle",
         "sample": f"{n_heads} of {w.BH} heads of {w.name}, forward + backward, float64 NumPy "
                   f"composed attention (it computes all S*S products; the rate uses the same "
-                  f"algorithmic flop count as the GPU); {dt:.1f} s on {platform.processor() or platform.machine()}",
+                  f"algorithmic flop count as the GPU); {dt:.1f} s on {_cpu_model()}",
         "seconds": round(dt, 2),
+        "fwd_seconds": round(t_fwd, 2),
+        "bwd_seconds": round(t_bwd, 2),
+        "fwd_tflops": round(w.fwd_flop * frac / t_fwd / 1e12, 6),
+        "bwd_tflops": round(w.bwd_flop * frac / t_bwd / 1e12, 6),
     }
 
 
@@ -211,7 +233,7 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=workloads.C4.name, choices=sorted(workloads.BY_NAME))
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=32)
+    ap.add_argument("--cpu-heads", type=int, default=64)
     ap.add_argument("--comparator", action="store_true",
                     help="also time composed attention (library GEMMs + softmax) and both paths' peak memory")
     ap.add_argument("--graph", action="store_true",
@@ -230,7 +252,8 @@ def main(argv=None):
 
     w = workloads.BY_NAME[args.workload]
     x = workloads.make_inputs(w)
-    ms_step, ms_mean, ms_med, device = gpu_bench(x, args.steps, args.warmup)
+    ms_step, stats, device = gpu_bench(x, args.steps, args.warmup)
+    ms_mean, ms_med, ms_min = stats["mean"], stats["median"], stats["min"]
     flop = w.fwd_flop + w.bwd_flop
     value = flop / (ms_step * 1e-3) / 1e12
 
@@ -249,13 +272,13 @@ def main(argv=None):
     pre_bytes = w.BH * w.S * (2 * w.hd * el + 4)   # read O, dO; write D
     phases = {
         "fwd": {"kernel": KERNEL_NAME["fwd"], "avg_ms": round(ms_mean["fwd"], 4), "median_ms": round(ms_med["fwd"], 4),
-                "tflops": round(w.fwd_flop / (ms_mean["fwd"] * 1e-3) / 1e12, 2)},
+                "min_ms": round(ms_min["fwd"], 4), "tflops": round(w.fwd_flop / (ms_mean["fwd"] * 1e-3) / 1e12, 2)},
         "bwd_preprocess": {"kernel": KERNEL_NAME["pre"], "avg_ms": round(ms_mean["pre"], 4),
-                           "median_ms": round(ms_med["pre"], 4),
+                           "median_ms": round(ms_med["pre"], 4), "min_ms": round(ms_min["pre"], 4),
                            "gbs": round(pre_bytes / (ms_mean["pre"] * 1e-3) / 1e9, 1),
                            "frac_hbm": round(pre_bytes / (ms_mean["pre"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
         "bwd": {"kernel": KERNEL_NAME["bwd"], "avg_ms": round(ms_mean["bwd"], 4), "median_ms": round(ms_med["bwd"], 4),
-                "tflops": round(w.bwd_flop / (ms_mean["bwd"] * 1e-3) / 1e12, 2)},
+                "min_ms": round(ms_min["bwd"], 4), "tflops": round(w.bwd_flop / (ms_mean["bwd"] * 1e-3) / 1e12, 2)},
     }
     rec = {
         "metric": METRIC,
@@ -282,7 +305,8 @@ def main(argv=None):
         rec["graph"] = {"ms_per_step": round(g_ms, 4), "value": round(flop / (g_ms * 1e-3) / 1e12, 2),
                         "unit": "TFLOP/s", "note": "the same step captured once in a HIP graph and replayed"}
     if args.dropout:
-        d_step, d_mean, _, _ = gpu_bench(x, args.steps, args.warmup, dropout_p=args.dropout)
+        d_step, d_stats, _ = gpu_bench(x, args.steps, args.warmup, dropout_p=args.dropout)
+        d_mean = d_stats["mean"]
         rec["dropout"] = {
             "p": args.dropout, "kernels": "fwd_kernel, bwd_key_kernel + bwd_query_kernel with in-kernel keep bits",
             "ms_per_step": round(d_step, 4), "fwd_ms": round(d_mean["fwd"], 4), "bwd_ms": round(d_mean["bwd"], 4),
