@@ -1,7 +1,7 @@
 """Throughput of the fused causal attention path on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--comparator]
-                    [--dropout P] [--graph]
+                    [--dropout P] [--graph] [--autograd]
 
 One step is one pass of the whole path over one batch: xfa_fwd, then
 xfa_bwd_preprocess, then xfa_bwd, with inputs resident in HBM.  The default
@@ -16,7 +16,10 @@ memory.  --dropout P adds the same step with dropout on the attention
 probabilities (xfa_fwd_dropout / xfa_bwd_dropout) and its cost over the plain
 step; the headline value is always the plain step.  --graph adds the step
 captured once in a HIP graph and replayed (the same kernels, without the
-per-launch host overhead that dominates the small workloads).
+per-launch host overhead that dominates the small workloads).  --autograd
+adds the differentiable op (flash_attention, forward then backward through
+torch autograd) in its native mode and in the fp32-core mode (bf16 tensors
+cast at the boundary, the fp32 kernels inside).
 """
 
 from __future__ import annotations
@@ -175,6 +178,47 @@ def graph_bench(x, steps: int, warmup: int):
     return (time.perf_counter() - t0) * 1e3 / steps
 
 
+def autograd_bench(x, steps: int, warmup: int, core: str):
+    """Mean fwd and bwd ms of flash_attention(...).backward() on x, for one core mode."""
+    import torch
+
+    import transformer_attention_xfa_amd as xfa
+
+    w = x.w
+    dev = torch.device("cuda", 0)
+    if w.dtype == "bf16":
+        q, k, v, do = (torch.from_numpy(getattr(x, n + "_bits").view(np.int16)).view(torch.bfloat16).to(dev)
+                       for n in ("q", "k", "v", "do"))
+    else:
+        q, k, v, do = (torch.from_numpy(getattr(x, n)).to(dev) for n in ("q", "k", "v", "do"))
+    q, k, v = (t.requires_grad_(True) for t in (q, k, v))
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        out = xfa.flash_attention(q, k, v, w.sm_scale, w.causal, core=core)
+        if ev is not None:
+            ev[1].record(stream)
+        out.backward(do)
+        if ev is not None:
+            ev[2].record(stream)
+        q.grad = k.grad = v.grad = None
+
+    for _ in range(warmup):
+        step()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    fwd = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
+    bwd = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
+    flop = w.fwd_flop + w.bwd_flop
+    return {"fwd_ms": round(fwd, 4), "bwd_ms": round(bwd, 4), "ms_per_step": round(fwd + bwd, 4),
+            "value": round(flop / ((fwd + bwd) * 1e-3) / 1e12, 2), "unit": "TFLOP/s"}
+
+
 def _cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -236,6 +280,8 @@ def main(argv=None):
     ap.add_argument("--cpu-heads", type=int, default=64)
     ap.add_argument("--comparator", action="store_true",
                     help="also time composed attention (library GEMMs + softmax) and both paths' peak memory")
+    ap.add_argument("--autograd", action="store_true",
+                    help="also time flash_attention forward + backward through autograd, native and fp32-core modes")
     ap.add_argument("--graph", action="store_true",
                     help="also time the plain step captured in a HIP graph and replayed")
     ap.add_argument("--dropout", type=float, default=0.0, metavar="P",
@@ -300,6 +346,16 @@ def main(argv=None):
         "phases": phases,
         "device": device,
     }
+    if args.autograd:
+        nat = autograd_bench(x, args.steps, args.warmup, "native")
+        f32 = autograd_bench(x, args.steps, args.warmup, "fp32")
+        f32["frac_of_fp32_peak"] = round(f32["value"] / PEAK_TFLOPS["f32"], 4)
+        rec["autograd"] = {
+            "op": "flash_attention(q, k, v).backward(dout), events around forward and backward",
+            "native": nat,
+            "fp32_core": dict(f32, note="bf16 tensors cast to fp32 at the boundary, fp32 kernels inside, "
+                                        "results cast back; the rate uses the same algorithmic flops"),
+        }
     if args.graph:
         g_ms = graph_bench(x, args.steps, args.warmup)
         rec["graph"] = {"ms_per_step": round(g_ms, 4), "value": round(flop / (g_ms * 1e-3) / 1e12, 2),
