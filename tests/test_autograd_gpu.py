@@ -157,3 +157,12 @@ def test_fp32_core_mode(B, H, S, hd, causal):
         assert errs["fp32"][name] <= 2.0 ** -7, (name, errs["fp32"])
     for name in errs["fp32"]:
         assert errs["fp32"][name] <= errs["native"][name] * 1.05 + 1e-6, (name, errs)
+
+
+def test_double_backward_is_refused():
+    # the backward is not itself differentiable: asking for it raises instead of returning wrong values
+    q, k, v = (torch.randn(1, 1, 64, 32, device="cuda", requires_grad=True) for _ in range(3))
+    out = xfa.flash_attention(q, k, v)
+    g, = torch.autograd.grad(out.sum(), q, create_graph=True)
+    with pytest.raises(RuntimeError):
+        g.sum().backward()

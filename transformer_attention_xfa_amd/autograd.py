@@ -42,6 +42,7 @@ class FlashAttentionFn(torch.autograd.Function):
         return out, lse
 
     @staticmethod
+    @torch.autograd.function.once_differentiable
     def backward(ctx, dout, _dlse):
         q, k, v, out, lse = ctx.saved_tensors
         if ctx.fp32_core:
