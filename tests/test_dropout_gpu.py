@@ -229,3 +229,26 @@ def test_autograd_with_dropout():
         for got, ref in ((qd.grad, dq_r), (kd.grad, dk_r), (vd.grad, dv_r)):
             g = got[b, h].cpu().double().numpy()
             assert np.abs(g - ref).max() <= 1e-4 * max(np.abs(ref).max(), 1e-2)
+
+
+def test_autograd_dropout_bf16_native_and_fp32_core():
+    # bf16 tensors through the op with dropout, in both modes, against the oracle on the same mask
+    B, H, S, hd, p, seed = 1, 2, 257, 128, 0.15, 31337
+    gen = torch.Generator().manual_seed(9)
+    q, k, v = (torch.randn(B, H, S, hd, generator=gen).to(torch.bfloat16) for _ in range(3))
+    do = (torch.randn(B, H, S, hd, generator=gen) * 0.1).to(torch.bfloat16)
+    scale = 1.0 / math.sqrt(hd)
+    for core in ("native", "fp32"):
+        qd, kd, vd = (t.cuda().requires_grad_(True) for t in (q, k, v))
+        out = xfa.flash_attention(qd, kd, vd, causal=True, dropout_p=p, seed=seed, core=core)
+        out.backward(do.cuda())
+        for bh in range(B * H):
+            b, h = divmod(bh, H)
+            args = [t[b, h].double().numpy() for t in (q, k, v)]
+            out_r, _ = attention_dropout_forward_head(*args, scale, True, p, seed, bh)
+            grads_r = attention_dropout_backward_head(*args, do[b, h].double().numpy(), scale, True, p, seed, bh)[:3]
+            e_out = np.abs(out[b, h].detach().float().cpu().numpy() - out_r).max()
+            errs = [np.linalg.norm(g[b, h].float().cpu().numpy() - r) / np.linalg.norm(r)
+                    for g, r in zip((qd.grad, kd.grad, vd.grad), grads_r)]
+            say(f"dropout autograd core={core} head {bh}: out {e_out:.3g} grads " + " ".join(f"{e:.3g}" for e in errs))
+            assert e_out <= 2e-2 and max(errs) <= 5e-2
