@@ -25,3 +25,8 @@ from ._binding import (  # noqa: F401
 )
 
 from .autograd import CORES, FlashAttentionFn, flash_attention  # noqa: E402,F401
+
+# short names: out, lse = fwd(q, k, v, scale=None, causal=True);
+# dq, dk, dv = bwd(q, k, v, out, dout, lse, scale=None, causal=True)
+fwd = forward
+bwd = backward
