@@ -680,12 +680,12 @@ __global__ __launch_bounds__((BwdCfg<T, HD>::NW * 64), 1) void bwd_key_kernel(Bw
 // register file: one workgroup per CU)
 template <typename T, int HD, bool DROP>
 __global__ __launch_bounds__((BwdCfg<T, HD>::NW * 64), (sizeof(T) == 2 && !DROP ? 2 : 1)) void bwd_query_kernel(
-    BwdParams<T> p, int nqq, int nwg) {
+    BwdParams<T> p, int nqq, int nwg, int BH) {
   using C = BwdCfg<T, HD>;
   __shared__ __attribute__((aligned(16))) char smem[C::QUERY_BYTES];
-  const int lid = xcd_logical(blockIdx.x, nwg);
-  const int bh = lid / nqq;
-  query_role<T, HD, C::NW, DROP>(p, bh, nqq - 1 - (lid - bh * nqq), smem);
+  int bh, rank;
+  pair_order(xcd_logical(blockIdx.x, nwg), nqq, BH, bh, rank);
+  query_role<T, HD, C::NW, DROP>(p, bh, nqq - 1 - rank, smem);
 }
 
 template <typename T, int HD>
@@ -705,9 +705,9 @@ static hipError_t launch_bwd_t(const BwdArgs& a) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.drop.thresh)
-    hipLaunchKernelGGL((bwd_query_kernel<T, HD, true>), dim3(nq), dim3(C::NW * 64), 0, a.stream, p, nqq, nq);
+    hipLaunchKernelGGL((bwd_query_kernel<T, HD, true>), dim3(nq), dim3(C::NW * 64), 0, a.stream, p, nqq, nq, (int)a.BH);
   else
-    hipLaunchKernelGGL((bwd_query_kernel<T, HD, false>), dim3(nq), dim3(C::NW * 64), 0, a.stream, p, nqq, nq);
+    hipLaunchKernelGGL((bwd_query_kernel<T, HD, false>), dim3(nq), dim3(C::NW * 64), 0, a.stream, p, nqq, nq, (int)a.BH);
   return hipGetLastError();
 }
 

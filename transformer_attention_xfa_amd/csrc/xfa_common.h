@@ -187,4 +187,25 @@ __device__ inline int xcd_logical(int bid, int n) {
   return x * q + (x < r ? x : r) + slot;
 }
 
+// Logical order of the query-tile workgroups (forward, backward query role):
+// heads are taken in pairs and the tiles of the two heads interleaved,
+// heaviest first (rank 0 = the tile with the most causal work); an odd last
+// head runs alone.  Two workgroups share each CU, so an XCD runs two heads at
+// once; dispatching each head's tiles heaviest first on its own would leave
+// the light tiles of both heads finishing together and the next pair's heavy
+// tiles starting late (a ~10 % tail in a greedy-dispatch model of one XCD),
+// while one longest-first list per pair keeps the slots level and still
+// confines the streamed K/V (or K/V/dO) to two heads per L2.
+__device__ inline void pair_order(int lid, int nt, int BH, int& bh, int& rank) {
+  const int pair = lid / (2 * nt);
+  const int r = lid - pair * 2 * nt;
+  if (2 * pair + 1 < BH) {
+    bh = 2 * pair + (r & 1);
+    rank = r >> 1;
+  } else {
+    bh = 2 * pair;
+    rank = r;
+  }
+}
+
 }  // namespace xfa
