@@ -1,6 +1,9 @@
 """Pins of the dropout oracle (oracle/dropout.py) to results fixed
 independently of its code:
-  * the generator's published reference outputs (splitmix64 from state 0);
+  * the generator's published reference outputs (splitmix64 from state 0),
+    and through them the keep decision of chosen (seed, index) pairs: the
+    index times the golden increment, the XOR with the seed and the 24-bit
+    window >> 40 are each fixed by the same outputs;
   * the keep rate and the uniformity of u over many indices (binomial and
     chi-square bounds);
   * p = 0 reduces exactly to plain attention;
@@ -30,6 +33,39 @@ def test_splitmix64_reference_outputs():
     states = np.array([0, golden, (2 * golden) % 2**64], dtype=np.uint64)
     got = [int(x) for x in splitmix64(states)]
     assert got == [0xE220A8397B1DCDAF, 0x6E789E6AA1B965F4, 0x06C45D188009454F]
+
+
+# splitmix64's first three outputs from state 0 (published with the
+# generator).  With seed 0 the key of index i is i * golden, which is the
+# generator's state after i steps, so h(0, i) is its output number i + 1.
+SPLITMIX_FIRST = (0xE220A8397B1DCDAF, 0x6E789E6AA1B965F4, 0x06C45D188009454F)
+GOLDEN = 0x9E3779B97F4A7C15
+
+
+def _keep_cases():
+    """(seed, index, u) triples whose u follows from the published outputs
+    alone: u = (output >> 40) / 2^24 of the output the key selects."""
+    u = [(h >> 40) / float(1 << 24) for h in SPLITMIX_FIRST]
+    cases = [(0, i, u[i]) for i in range(3)]
+    # seed XOR index*golden selects the state: seed golden at index 1 gives
+    # key 0 (output 1); seed (golden XOR 2 golden) at index 1 gives key
+    # 2 golden (output 3), which an addition in place of the XOR would miss
+    g2 = (2 * GOLDEN) % 2**64
+    cases += [(GOLDEN, 1, u[0]), (GOLDEN ^ g2, 1, u[2]), (g2, 2, u[0])]
+    return cases
+
+
+@pytest.mark.parametrize("seed,index,u", _keep_cases())
+def test_keep_decision_at_published_outputs(seed, index, u):
+    # u = k / 2^24 is exact in float32; keep iff u >= p
+    u32 = np.float32(u)
+    assert float(u32) == u
+    below = np.nextafter(u32, np.float32(0))
+    above = np.nextafter(u32, np.float32(1))
+    idx = np.array([index], dtype=np.uint64)
+    assert keep_mask(seed, idx, float(below))[0]
+    assert keep_mask(seed, idx, float(u32))[0]
+    assert not keep_mask(seed, idx, float(above))[0]
 
 
 @pytest.mark.parametrize("p", [0.1, 0.5, 0.9])

@@ -6,7 +6,8 @@ mask, log base, sign, a generator constant), on the CPU, and checks that the
 pins fail on the copy while they pass on the unmodified source.  The pins
 used here are the same independent references as in test_oracle_pins.py and
 test_dropout_oracle_pins.py: the pure-Python brute force, splitmix64's
-published outputs, the keep rate, and the unbiasedness of inverted dropout.
+published outputs and the keep decisions they fix, the keep rate, and the
+unbiasedness of inverted dropout.
 The oracle files themselves are never modified.
 """
 
@@ -60,6 +61,14 @@ def dropout_pins_pass(m):
     states = np.array([0, golden, (2 * golden) % 2**64], dtype=np.uint64)
     if [int(x) for x in m.splitmix64(states)] != [0xE220A8397B1DCDAF, 0x6E789E6AA1B965F4, 0x06C45D188009454F]:
         return False
+    # keep decisions at indices whose u the published outputs fix
+    from tests.test_dropout_oracle_pins import _keep_cases
+    for seed, index, u in _keep_cases():
+        u32 = np.float32(u)
+        idx = np.array([index], dtype=np.uint64)
+        if not (m.keep_mask(seed, idx, float(u32))[0]
+                and not m.keep_mask(seed, idx, float(np.nextafter(u32, np.float32(1))))[0]):
+            return False
     n, p = 1 << 16, 0.3
     keep = m.keep_mask(2024, np.arange(n, dtype=np.uint64), p)
     if abs(keep.sum() - n * (1 - p)) > 5 * math.sqrt(n * p * (1 - p)):
@@ -117,6 +126,12 @@ DROPOUT_SLIPS = {
     "mask left out of dV": ("dv += (pr * m).T @ do_rows", "dv += pr.T @ do_rows"),
     "mask left out of dP": ("dp = m * (do_rows @ v.T)", "dp = do_rows @ v.T"),
     "dropped scale in the dropout backward": ("g = pr * (dp - rs[:, None]) * scale", "g = pr * (dp - rs[:, None])"),
+    "index not multiplied by golden": ("key = np.uint64(seed & 0xFFFFFFFFFFFFFFFF) ^ (idx * GOLDEN)",
+                                       "key = np.uint64(seed & 0xFFFFFFFFFFFFFFFF) ^ idx"),
+    "addition in place of XOR": ("key = np.uint64(seed & 0xFFFFFFFFFFFFFFFF) ^ (idx * GOLDEN)",
+                                 "key = np.uint64(seed & 0xFFFFFFFFFFFFFFFF) + (idx * GOLDEN)"),
+    "low 24 bits in place of the top 24": ("u = (h >> np.uint64(40)).astype(np.float32)",
+                                           "u = (h & np.uint64(0xFFFFFF)).astype(np.float32)"),
     "index rows and keys swapped": ("idx = (np.uint64(bh) * np.uint64(S) + i) * np.uint64(S) + j",
                                     "idx = (np.uint64(bh) * np.uint64(S) + j) * np.uint64(S) + i"),
 }
