@@ -230,43 +230,83 @@ def _cpu_model() -> str:
     return platform.processor() or platform.machine()
 
 
-def cpu_baseline(x, n_heads: int):
-    """The oracle, untuned, on the first n_heads heads of the workload (fwd + bwd)."""
+# The host share of one GPU on the measurement machines: worker pools stay
+# within it whatever the affinity mask shows.
+HOST_WORKERS_MAX = 16
+_BLAS_ENV = ("OPENBLAS_NUM_THREADS", "OMP_NUM_THREADS", "MKL_NUM_THREADS")
+
+
+def _oracle_job(job):
+    """One head of the oracle in a pool worker: (phase, q, k, v, do, scale, causal) -> seconds."""
     from oracle import attention_backward_head, attention_forward_head
+
+    phase, q, k, v, do, scale, causal = job
+    t0 = time.perf_counter()
+    if phase == "fwd":
+        attention_forward_head(q, k, v, scale, causal, row_block=1024)
+    else:
+        attention_backward_head(q, k, v, do, scale, causal, row_block=1024)
+    return time.perf_counter() - t0
+
+
+def _oracle_ready(_):
+    import oracle  # noqa: F401  (imports done before the timed maps)
+    time.sleep(0.25)   # long enough that every worker takes one of these
+    return os.getpid()
+
+
+def cpu_baseline(x, n_heads: int):
+    """The oracle, untuned, on the first n_heads heads of the workload, one
+    head per task in a pool of single-threaded worker processes (one per
+    available host core, at most HOST_WORKERS_MAX); the forward of all
+    sampled heads, then their backward, each timed as wall time around the
+    pool's map.  Workers are started fresh (spawn) with one BLAS thread; a
+    worker that dies breaks the pool with an error instead of a hang."""
+    import multiprocessing as mp
+    from concurrent.futures import ProcessPoolExecutor
 
     w = x.w
     n_heads = max(1, min(n_heads, w.BH))
-    cores = None
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max((i.get("num_threads") or 0) for i in threadpool_info()) or None
-    except Exception:
-        pass
+    workers = max(1, min(len(os.sched_getaffinity(0)), HOST_WORKERS_MAX, n_heads))
     heads = [[x.f64(n, h) for n in ("q", "k", "v", "do")] for h in range(n_heads)]
-    t_fwd = t_bwd = 0.0
-    for q, k, v, do in heads:
-        t0 = time.perf_counter()
-        attention_forward_head(q, k, v, w.sm_scale, w.causal, row_block=1024)
-        t1 = time.perf_counter()
-        attention_backward_head(q, k, v, do, w.sm_scale, w.causal, row_block=1024)
-        t_fwd += t1 - t0
-        t_bwd += time.perf_counter() - t1
+    saved = {k: os.environ.get(k) for k in _BLAS_ENV}
+    os.environ.update({k: "1" for k in _BLAS_ENV})   # inherited by the spawned workers
+    try:
+        with ProcessPoolExecutor(workers, mp_context=mp.get_context("spawn")) as pool:
+            pids = set(pool.map(_oracle_ready, range(workers), timeout=300))
+            wall = {}
+            busy = {}
+            for phase in ("fwd", "bwd"):
+                jobs = [(phase, q, k, v, do, w.sm_scale, w.causal) for q, k, v, do in heads]
+                t0 = time.perf_counter()
+                per_head = list(pool.map(_oracle_job, jobs, timeout=900))
+                wall[phase] = time.perf_counter() - t0
+                busy[phase] = float(sum(per_head))
+    finally:
+        for k, val in saved.items():
+            if val is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = val
+    t_fwd, t_bwd = wall["fwd"], wall["bwd"]
     dt = t_fwd + t_bwd
     frac = n_heads / w.BH
     flop = (w.fwd_flop + w.bwd_flop) * frac
     return {
         "value": round(flop / dt / 1e12, 6),
         "unit": "TFLOP/s",
-        "cores": cores or os.cpu_count(),
+        "cores": workers,
         "kind": "oracle",
-        "sample": f"{n_heads} of {w.BH} heads of {w.name}, forward + backward, float64 NumPy "
-                  f"composed attention (it computes all S*S products; the rate uses the same "
-                  f"algorithmic flop count as the GPU); {dt:.1f} s on {_cpu_model()}",
+        "sample": f"{n_heads} of {w.BH} heads of {w.name}, forward then backward, float64 NumPy composed "
+                  f"attention (it computes all S*S products; the rate uses the same algorithmic flop count "
+                  f"as the GPU), one head per task on a pool of {workers} single-threaded worker processes "
+                  f"({len(pids)} started), wall time {dt:.1f} s on {_cpu_model()}",
         "seconds": round(dt, 2),
         "fwd_seconds": round(t_fwd, 2),
         "bwd_seconds": round(t_bwd, 2),
         "fwd_tflops": round(w.fwd_flop * frac / t_fwd / 1e12, 6),
         "bwd_tflops": round(w.bwd_flop * frac / t_bwd / 1e12, 6),
+        "worker_busy_seconds": round(busy["fwd"] + busy["bwd"], 2),
     }
 
 
@@ -277,7 +317,8 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=workloads.C4.name, choices=sorted(workloads.BY_NAME))
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=64)
+    ap.add_argument("--cpu-heads", type=int, default=32,
+                    help="heads of the workload the CPU oracle runs (default 32: a quarter of C4, 10-20 s)")
     ap.add_argument("--comparator", action="store_true",
                     help="also time composed attention (library GEMMs + softmax) and both paths' peak memory")
     ap.add_argument("--autograd", action="store_true",
@@ -298,6 +339,8 @@ def main(argv=None):
 
     w = workloads.BY_NAME[args.workload]
     x = workloads.make_inputs(w)
+    # the oracle's worker pool runs before this process touches the GPU
+    cpu = None if args.no_cpu_baseline else cpu_baseline(x, args.cpu_heads)
     ms_step, stats, device = gpu_bench(x, args.steps, args.warmup)
     ms_mean, ms_med, ms_min = stats["mean"], stats["median"], stats["min"]
     flop = w.fwd_flop + w.bwd_flop
@@ -374,8 +417,8 @@ def main(argv=None):
     if args.comparator:
         import comparator
         rec["comparator"] = comparator.comparator_record(x, max(1, args.steps // 4), 1, ms_step)
-    if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(x, args.cpu_heads)
+    if cpu is not None:
+        rec["cpu_baseline"] = cpu
     print(json.dumps(rec), flush=True)
     return 0
 

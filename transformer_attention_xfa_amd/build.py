@@ -38,7 +38,6 @@ def hipcc() -> str:
 
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
-    "-munsafe-fp-atomics",
     # keep the compiler from forming packed fp32 VALU ops
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",

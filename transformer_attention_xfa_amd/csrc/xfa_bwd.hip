@@ -24,16 +24,20 @@
 // workspace, and dQ is bitwise reproducible.
 //
 // Pipeline.  The streamed 32-row blocks (Q, dO, L, D for a key workgroup;
-// K, V for a query workgroup) rotate through three LDS buffers, and two
-// staged blocks are in flight in registers, so a global load has more than an
-// iteration to land.  In a key workgroup (one wave per SIMD), iteration n
-// (one workgroup barrier) forms the two score contractions of block n+1,
-// writes block n+2 into the buffer block n-1 used, finishes block n
-// (exponentials, dS and the gradient contractions) and issues the loads of
-// block n+4; the score contractions of n+1 do not depend on block n's
-// exponentials, so the matrix cores have work while the vector units
-// evaluate them.  A query workgroup runs two waves per SIMD instead and
-// finishes each block in its own iteration.
+// K, V for a query workgroup) rotate through four LDS buffers filled by DMA
+// (buffer loads that write LDS, xfa_stage.h), so no registers hold staged
+// data: block m+3 is fetched at the start of iteration m into the buffer
+// block m-1 used, a block has more than an iteration to land, and one
+// `s_waitcnt vmcnt` plus one workgroup barrier end each iteration.  In a key
+// workgroup (one wave per SIMD), bf16 iteration n forms the two score
+// contractions of block n+1 interleaved with the exponentials and dS of
+// block n, then block n's u = 0 gradient contractions; its u = 1 gradient
+// contractions run at the start of iteration n+1 from operands carried in
+// registers across the barrier.  The score contractions of n+1 do not depend
+// on block n's exponentials, so the matrix cores have work while the vector
+// units evaluate them.  A query workgroup runs two waves per SIMD and
+// interleaves the same way (scores of block n+1 between the exponentials and
+// transposed K reads of block n, then block n's dQ contractions).
 //
 // The operands whose contraction index runs along block rows (dO^T and Q^T
 // for the key workgroups, K^T for the query workgroups) are read from the

@@ -1,6 +1,7 @@
-// Streaming of 32-row blocks of [S][HD] tensors from HBM into LDS for the
-// backward kernels: the LDS layout of a block, its operand reads, the DMA
-// that fills it, and the parity runner of the hand-unrolled loops.
+// Streaming of 32-row blocks of [S][HD] tensors from HBM into LDS, shared by
+// the forward and both backward kernels: the LDS layout of a block, its
+// operand reads, the DMA that fills it, and the parity runner of the
+// hand-unrolled loops.
 #pragma once
 
 #include <type_traits>
