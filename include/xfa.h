@@ -83,20 +83,37 @@ xfa_status_t xfa_bwd_preprocess(const void* out, const void* dout, float* delta,
                                 int64_t B, int64_t H, int64_t S, int64_t hd, float scale,
                                 int causal, int dtype, void* stream);
 
+/* Device workspace xfa_bwd and xfa_bwd_dropout need for a shape, in bytes
+ * (T14 design doc, "Module Layout": the backward FFI entry next to the
+ * forward's; "Key Design Decisions" 3 and the escape hatches: dQ summed per
+ * query row, dK/dV per key block).  dQ can be summed across key blocks by
+ * fp32 atomics into such a workspace or formed by a separate query-outer
+ * pass that owns its rows; this library ships the second (the minimum atomic
+ * traffic of the first alone takes longer than the whole backward on
+ * MI355X), so the result is 0 for every shape and dtype and the workspace
+ * argument is never dereferenced.  Pure function of its arguments, no GPU
+ * call; arguments are validated by xfa_bwd, not here.                       */
+size_t xfa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t S, int64_t hd, int dtype);
+
 /* Backward (T14 design doc, "What flash-attention is", backward part:
  * p = exp(s - L), dp = dO . V, ds = p (dp - D) scale; dQ += ds K,
  * dK += ds Q, dV += p dO).
  *   in : q, k, v, dout [B,H,S,hd] dtype; lse [B,H,S] from xfa_fwd;
  *        delta [B,H,S] from xfa_bwd_preprocess
  *   out: dq, dk, dv    [B,H,S,hd] dtype (fully overwritten)
- * Two kernels on `stream` (dK/dV, then dQ), no scratch memory.  Each output
- * element is produced by exactly one workgroup (no atomics), so results are
- * bitwise reproducible.  On XFA_ERR_HIP the dK/dV kernel may have been
- * enqueued already; the outputs are then unspecified.                        */
+ *   workspace          caller-owned device memory of at least
+ *                      xfa_bwd_workspace_bytes(B, H, S, hd, dtype) bytes,
+ *                      256-byte aligned, overlapping no other argument; may
+ *                      be NULL when that size is 0 (always, in this build),
+ *                      and is then not dereferenced.
+ * Two kernels on `stream` (dK/dV, then dQ).  Each output element is produced
+ * by exactly one workgroup (no atomics), so results are bitwise
+ * reproducible.  On XFA_ERR_HIP the dK/dV kernel may have been enqueued
+ * already; the outputs are then unspecified.                                */
 xfa_status_t xfa_bwd(const void* q, const void* k, const void* v, const void* dout,
                      const float* lse, const float* delta, void* dq, void* dk, void* dv,
-                     int64_t B, int64_t H, int64_t S, int64_t hd, float scale, int causal,
-                     int dtype, void* stream);
+                     void* workspace, int64_t B, int64_t H, int64_t S, int64_t hd, float scale,
+                     int causal, int dtype, void* stream);
 
 /* Dropout on the attention probabilities (xtrain dropout design doc, section
  * "RNG: counter-based"; applied to P as inverted dropout): with
@@ -115,15 +132,17 @@ xfa_status_t xfa_bwd(const void* q, const void* k, const void* v, const void* do
  *              runs the kernels without dropout (bitwise the plain calls).
  *   seed       any 64-bit value; the forward and the backward of one step
  *              must get the same seed, p, B, H, S.
- * Other arguments, layouts and errors as in xfa_fwd and xfa_bwd.            */
+ * Other arguments (the workspace included), layouts and errors as in xfa_fwd
+ * and xfa_bwd.                                                               */
 xfa_status_t xfa_fwd_dropout(const void* q, const void* k, const void* v, void* out, float* lse,
                              int64_t B, int64_t H, int64_t S, int64_t hd, float scale, int causal,
                              float dropout_p, uint64_t seed, int dtype, void* stream);
 
 xfa_status_t xfa_bwd_dropout(const void* q, const void* k, const void* v, const void* dout,
                              const float* lse, const float* delta, void* dq, void* dk, void* dv,
-                             int64_t B, int64_t H, int64_t S, int64_t hd, float scale, int causal,
-                             float dropout_p, uint64_t seed, int dtype, void* stream);
+                             void* workspace, int64_t B, int64_t H, int64_t S, int64_t hd,
+                             float scale, int causal, float dropout_p, uint64_t seed, int dtype,
+                             void* stream);
 
 /* Static, NUL-terminated description of a status code.                       */
 const char* xfa_status_string(xfa_status_t status);

@@ -24,8 +24,8 @@ def _declared():
 
 def test_library_exports_every_declared_symbol():
     names = _declared()
-    assert names == sorted(["xfa_fwd", "xfa_bwd_preprocess", "xfa_bwd", "xfa_fwd_dropout", "xfa_bwd_dropout",
-                            "xfa_status_string"])
+    assert names == sorted(["xfa_fwd", "xfa_bwd_preprocess", "xfa_bwd", "xfa_bwd_workspace_bytes",
+                            "xfa_fwd_dropout", "xfa_bwd_dropout", "xfa_status_string"])
     lib = ctypes.CDLL(xfa.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -56,7 +56,7 @@ def _bwd(**kw):
              B=1, H=2, S=64, hd=64, scale=0.125, causal=1, dtype=1)
     a.update(kw)
     return xfa.lib().xfa_bwd(a["q"], a["k"], a["v"], a["dout"], a["lse"], a["delta"], a["dq"],
-                             a["dk"], a["dv"], a["B"], a["H"], a["S"], a["hd"], a["scale"],
+                             a["dk"], a["dv"], a.get("ws"), a["B"], a["H"], a["S"], a["hd"], a["scale"],
                              a["causal"], a["dtype"], None)
 
 
@@ -72,8 +72,8 @@ def _bwd_drop(**kw):
              B=1, H=2, S=64, hd=64, scale=0.125, causal=1, p=0.1, seed=7, dtype=1)
     a.update(kw)
     return xfa.lib().xfa_bwd_dropout(a["q"], a["k"], a["v"], a["dout"], a["lse"], a["delta"], a["dq"],
-                                     a["dk"], a["dv"], a["B"], a["H"], a["S"], a["hd"], a["scale"],
-                                     a["causal"], a["p"], a["seed"], a["dtype"], None)
+                                     a["dk"], a["dv"], a.get("ws"), a["B"], a["H"], a["S"], a["hd"],
+                                     a["scale"], a["causal"], a["p"], a["seed"], a["dtype"], None)
 
 
 @pytest.mark.parametrize("call", [_fwd, _pre, _bwd, _fwd_drop, _bwd_drop])
@@ -169,3 +169,22 @@ def test_flash_attention_rejects_bad_dropout_probability(p):
     t = torch.zeros(1, 1, 4, 16)
     with pytest.raises(ValueError, match="dropout_p"):
         xfa.flash_attention(t, t, t, dropout_p=p)
+
+
+@pytest.mark.parametrize("dtype", [0, 1])
+@pytest.mark.parametrize("B,H,S,hd", [(1, 1, 64, 16), (8, 16, 4096, 128), (1, 32, 16384, 128), (2, 3, 1, 64),
+                                      (0, 4, 100, 32)])
+def test_workspace_bytes_is_zero(B, H, S, hd, dtype):
+    # the shipped backward forms dQ in its own query-outer kernel: no
+    # workspace for any shape, so NULL is a valid workspace argument
+    assert xfa.lib().xfa_bwd_workspace_bytes(B, H, S, hd, dtype) == 0
+    assert xfa.xfa_bwd_workspace_bytes(B, H, S, hd, dtype) == 0
+
+
+def test_workspace_pointer_is_not_checked_when_size_is_zero():
+    # with no workspace needed, NULL and any other value pass the checks
+    # (an empty problem returns before any GPU call)
+    assert _bwd(ws=None, S=0) == OK
+    assert _bwd(ws=A, S=0) == OK
+    assert _bwd_drop(ws=None, S=0) == OK
+    assert _bwd(ws=None, hd=48) == UNSUP

@@ -19,6 +19,7 @@ from ._binding import (  # noqa: F401
     xfa_bwd,
     xfa_bwd_dropout,
     xfa_bwd_preprocess,
+    xfa_bwd_workspace_bytes,
     xfa_fwd,
     xfa_fwd_dropout,
     xfa_status_string,

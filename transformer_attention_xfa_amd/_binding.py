@@ -25,9 +25,10 @@ _c_void_p, _i64, _f32, _int, _u64 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_fl
 _SIGS = {
     "xfa_fwd": (_int, [_c_void_p] * 5 + [_i64] * 4 + [_f32, _int, _int, _c_void_p]),
     "xfa_bwd_preprocess": (_int, [_c_void_p] * 3 + [_i64] * 4 + [_f32, _int, _int, _c_void_p]),
-    "xfa_bwd": (_int, [_c_void_p] * 9 + [_i64] * 4 + [_f32, _int, _int, _c_void_p]),
+    "xfa_bwd": (_int, [_c_void_p] * 10 + [_i64] * 4 + [_f32, _int, _int, _c_void_p]),
     "xfa_fwd_dropout": (_int, [_c_void_p] * 5 + [_i64] * 4 + [_f32, _int, _f32, _u64, _int, _c_void_p]),
-    "xfa_bwd_dropout": (_int, [_c_void_p] * 9 + [_i64] * 4 + [_f32, _int, _f32, _u64, _int, _c_void_p]),
+    "xfa_bwd_dropout": (_int, [_c_void_p] * 10 + [_i64] * 4 + [_f32, _int, _f32, _u64, _int, _c_void_p]),
+    "xfa_bwd_workspace_bytes": (ctypes.c_size_t, [_i64] * 4 + [_int]),
     "xfa_status_string": (ctypes.c_char_p, [_int]),
 }
 
@@ -109,6 +110,27 @@ def _raise(st: int, where: str):
         raise XfaError(st, where)
 
 
+def xfa_bwd_workspace_bytes(B: int, H: int, S: int, hd: int, dtype_code: int) -> int:
+    """Bytes of device workspace the backward needs for this shape (0 in this build)."""
+    return int(lib().xfa_bwd_workspace_bytes(B, H, S, hd, int(dtype_code)))
+
+
+def _workspace_ptr(q, workspace, where: str):
+    """Device address of the caller's workspace, checked against the size the
+    library asks for; None (NULL) when it asks for none."""
+    B, H, S, hd = q.shape
+    need = xfa_bwd_workspace_bytes(B, H, S, hd, _dtype_code(q))
+    if need == 0:
+        return None
+    if workspace is None:
+        raise ValueError(f"{where}: needs a device workspace of {need} bytes (xfa_bwd_workspace_bytes)")
+    if not workspace.is_cuda or workspace.device != q.device:
+        raise ValueError(f"{where}: workspace must be on {q.device}")
+    if workspace.numel() * workspace.element_size() < need or workspace.data_ptr() % 256:
+        raise ValueError(f"{where}: workspace must hold {need} bytes, 256-byte aligned")
+    return workspace.data_ptr()
+
+
 # ------------------------------------------------------ C-ABI entry points
 def xfa_fwd(q, k, v, out, lse, scale=None, causal=True, stream=None) -> None:
     """q, k, v, out: [B,H,S,hd] (float32 or bfloat16); lse: [B,H,S] float32."""
@@ -134,15 +156,18 @@ def xfa_bwd_preprocess(out, dout, delta, scale=None, causal=True, stream=None) -
     _raise(st, "xfa_bwd_preprocess")
 
 
-def xfa_bwd(q, k, v, dout, lse, delta, dq, dk, dv, scale=None, causal=True, stream=None) -> None:
-    """dq, dk, dv <- gradients of sum(dout * out)."""
+def xfa_bwd(q, k, v, dout, lse, delta, dq, dk, dv, scale=None, causal=True, stream=None,
+            workspace=None) -> None:
+    """dq, dk, dv <- gradients of sum(dout * out).  workspace: a device tensor
+    of at least xfa_bwd_workspace_bytes(...) bytes, or None when that is 0."""
     torch = _torch()
     B, H, S, hd = q.shape
     _check_same(q, q, k, v, dout, dq, dk, dv, shape=q.shape, dtype=q.dtype,
                 names=("q", "k", "v", "dout", "dq", "dk", "dv"))
     _check_same(q, lse, delta, shape=(B, H, S), dtype=torch.float32, names=("lse", "delta"))
+    ws = _workspace_ptr(q, workspace, "xfa_bwd")
     st = lib().xfa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(), lse.data_ptr(),
-                       delta.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                       delta.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws,
                        B, H, S, hd, _scale(scale, hd), int(bool(causal)), _dtype_code(q),
                        _stream_handle(stream))
     _raise(st, "xfa_bwd")
@@ -162,15 +187,16 @@ def xfa_fwd_dropout(q, k, v, out, lse, scale=None, causal=True, dropout_p=0.0, s
 
 
 def xfa_bwd_dropout(q, k, v, dout, lse, delta, dq, dk, dv, scale=None, causal=True, dropout_p=0.0, seed=0,
-                    stream=None) -> None:
+                    stream=None, workspace=None) -> None:
     """xfa_bwd of the forward that xfa_fwd_dropout ran with the same p and seed."""
     torch = _torch()
     B, H, S, hd = q.shape
     _check_same(q, q, k, v, dout, dq, dk, dv, shape=q.shape, dtype=q.dtype,
                 names=("q", "k", "v", "dout", "dq", "dk", "dv"))
     _check_same(q, lse, delta, shape=(B, H, S), dtype=torch.float32, names=("lse", "delta"))
+    ws = _workspace_ptr(q, workspace, "xfa_bwd_dropout")
     st = lib().xfa_bwd_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(), lse.data_ptr(),
-                               delta.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                               delta.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws,
                                B, H, S, hd, _scale(scale, hd), int(bool(causal)), float(dropout_p),
                                _seed(seed), _dtype_code(q), _stream_handle(stream))
     _raise(st, "xfa_bwd_dropout")
@@ -198,8 +224,10 @@ def backward(q, k, v, out, dout, lse, scale=None, causal=True, stream=None, drop
     delta = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
     xfa_bwd_preprocess(out, dout, delta, scale, causal, stream)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    need = xfa_bwd_workspace_bytes(B, H, S, hd, _dtype_code(q))
+    ws = torch.empty(need, dtype=torch.uint8, device=q.device) if need else None
     if dropout_p:
-        xfa_bwd_dropout(q, k, v, dout, lse, delta, dq, dk, dv, scale, causal, dropout_p, seed, stream)
+        xfa_bwd_dropout(q, k, v, dout, lse, delta, dq, dk, dv, scale, causal, dropout_p, seed, stream, ws)
     else:
-        xfa_bwd(q, k, v, dout, lse, delta, dq, dk, dv, scale, causal, stream)
+        xfa_bwd(q, k, v, dout, lse, delta, dq, dk, dv, scale, causal, stream, ws)
     return dq, dk, dv

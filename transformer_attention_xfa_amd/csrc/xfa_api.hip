@@ -101,10 +101,16 @@ xfa_status_t xfa_bwd_preprocess(const void* out, const void* dout, float* delta,
   return from_hip(xfa::launch_bwd_preprocess(a));
 }
 
+size_t xfa_bwd_workspace_bytes(int64_t, int64_t, int64_t, int64_t, int) {
+  // dQ is formed by its own query-outer kernel: nothing is accumulated
+  // across workgroups, so no workspace
+  return 0;
+}
+
 xfa_status_t xfa_bwd(const void* q, const void* k, const void* v, const void* dout,
                      const float* lse, const float* delta, void* dq, void* dk, void* dv,
-                     int64_t B, int64_t H, int64_t S, int64_t hd, float scale, int causal,
-                     int dtype, void* stream) {
+                     void* /*workspace: size 0, unused*/, int64_t B, int64_t H, int64_t S, int64_t hd,
+                     float scale, int causal, int dtype, void* stream) {
   Shape sh;
   xfa_status_t st = check_common(B, H, S, hd, scale, causal, dtype, &sh);
   if (st != XFA_OK || sh.empty) return st;
@@ -116,8 +122,9 @@ xfa_status_t xfa_bwd(const void* q, const void* k, const void* v, const void* do
 
 xfa_status_t xfa_bwd_dropout(const void* q, const void* k, const void* v, const void* dout,
                              const float* lse, const float* delta, void* dq, void* dk, void* dv,
-                             int64_t B, int64_t H, int64_t S, int64_t hd, float scale, int causal,
-                             float dropout_p, uint64_t seed, int dtype, void* stream) {
+                             void* /*workspace: size 0, unused*/, int64_t B, int64_t H, int64_t S,
+                             int64_t hd, float scale, int causal, float dropout_p, uint64_t seed,
+                             int dtype, void* stream) {
   Shape sh;
   xfa::DropArgs d;
   xfa_status_t st = check_common(B, H, S, hd, scale, causal, dtype, &sh);
