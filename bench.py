@@ -1,7 +1,7 @@
 """Throughput of the fused causal attention path on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--comparator]
-                    [--dropout P] [--graph] [--autograd]
+                    [--dropout P] [--graph] [--autograd] [--dq-atomic-floor]
 
 One step is one pass of the whole path over one batch: xfa_fwd, then
 xfa_bwd_preprocess, then xfa_bwd, with inputs resident in HBM.  The default
@@ -19,7 +19,9 @@ captured once in a HIP graph and replayed (the same kernels, without the
 per-launch host overhead that dominates the small workloads).  --autograd
 adds the differentiable op (flash_attention, forward then backward through
 torch autograd) in its native mode and in the fp32-core mode (bf16 tensors
-cast at the boundary, the fp32 kernels inside).
+cast at the boundary, the fp32 kernels inside).  --dq-atomic-floor adds the
+time of the fp32 atomic adds alone that summing dQ across key workgroups
+would take (comparator_kernels/dq_atomic_floor.hip), beside the backward.
 """
 
 from __future__ import annotations
@@ -317,14 +319,17 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=workloads.C4.name, choices=sorted(workloads.BY_NAME))
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=32,
-                    help="heads of the workload the CPU oracle runs (default 32: a quarter of C4, 10-20 s)")
+    ap.add_argument("--cpu-heads", type=int, default=128,
+                    help="heads of the workload the CPU oracle runs (default 128: all of C4's)")
     ap.add_argument("--comparator", action="store_true",
                     help="also time composed attention (library GEMMs + softmax) and both paths' peak memory")
     ap.add_argument("--autograd", action="store_true",
                     help="also time flash_attention forward + backward through autograd, native and fp32-core modes")
     ap.add_argument("--graph", action="store_true",
                     help="also time the plain step captured in a HIP graph and replayed")
+    ap.add_argument("--dq-atomic-floor", action="store_true",
+                    help="also time the fp32 atomic traffic alone that summing dQ across key workgroups "
+                         "would need (the alternative to the separate dQ kernel)")
     ap.add_argument("--dropout", type=float, default=0.0, metavar="P",
                     help="also time the step with dropout probability P on the attention probabilities")
     args = ap.parse_args(argv)
@@ -414,6 +419,9 @@ def main(argv=None):
             "fwd_cost_vs_plain": round(d_mean["fwd"] / ms_mean["fwd"], 3),
             "bwd_cost_vs_plain": round(d_mean["bwd"] / ms_mean["bwd"], 3),
         }
+    if args.dq_atomic_floor:
+        import comparator
+        rec["dq_atomic_floor"] = comparator.dq_atomic_floor_record(w, args.steps, ms_mean["bwd"])
     if args.comparator:
         import comparator
         rec["comparator"] = comparator.comparator_record(x, max(1, args.steps // 4), 1, ms_step)

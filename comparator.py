@@ -13,6 +13,11 @@ S x S tensors.  This is a comparator, not a second implementation of the op:
 it computes all S*S products where the fused op skips the masked half.
 Every batched product is given contiguous operands (the transposes are
 formed as small [.., hd, S] copies).
+
+dq_atomic_floor_record() times the other comparator in the same library
+(comparator_kernels/dq_atomic_floor.hip): the fp32 atomic traffic alone that
+summing dQ across key workgroups would need, the alternative to the fused
+op's separate query-outer dQ kernel.
 """
 from __future__ import annotations
 
@@ -41,6 +46,85 @@ def _softmax():
                        ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
         _softmax_lib = fn
     return _softmax_lib
+
+
+_floor_fn = None
+
+
+def _floor():
+    """xfa_comparator_dq_atomic_floor from comparator_kernels/libcomposed.so."""
+    global _floor_fn
+    if _floor_fn is None:
+        import ctypes
+
+        _softmax()                          # loads (or reports) the library
+        import os
+
+        path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "comparator_kernels", "libcomposed.so")
+        fn = ctypes.CDLL(path).xfa_comparator_dq_atomic_floor
+        fn.restype = ctypes.c_int
+        fn.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                       ctypes.c_void_p]
+        _floor_fn = fn
+    return _floor_fn
+
+
+def dq_atomic_floor(acc, causal):
+    """One launch of the atomic-floor kernel on a [B, H, S, hd] fp32 buffer."""
+    import torch
+
+    B, H, S, hd = acc.shape
+    assert acc.is_contiguous() and acc.dtype == torch.float32 and acc.is_cuda
+    st = _floor()(acc.data_ptr(), B * H, S, hd, int(bool(causal)), torch.cuda.current_stream().cuda_stream)
+    if st != 0:
+        raise RuntimeError(f"xfa_comparator_dq_atomic_floor failed (status {st})")
+
+
+def dq_atomic_floor_expected(S, hd, causal):
+    """acc[bh, q, d] after one launch on zeros: the key workgroups (128 keys)
+    that see query q."""
+    nkt = (S + 127) // 128
+    rows = (np.arange(S) // 128 + 1) if causal else np.full(S, nkt)
+    return np.repeat(rows[:, None].astype(np.float32), hd, axis=1)
+
+
+def dq_atomic_floor_record(w, steps, bwd_ms=None):
+    """Time of the minimum fp32 atomic traffic the atomic dQ design needs on
+    workload w, checked once for its counts; bwd_ms is the fused backward's
+    time for comparison."""
+    import torch
+
+    B, H, S, hd = w.shape
+    acc = torch.zeros((B, H, S, hd), dtype=torch.float32, device="cuda")
+    dq_atomic_floor(acc, w.causal)
+    torch.cuda.synchronize()
+    exp = torch.from_numpy(dq_atomic_floor_expected(S, hd, w.causal)).cuda()
+    ok = bool(torch.equal(acc, exp.expand_as(acc)))
+    stream = torch.cuda.current_stream()
+    times = []
+    for _ in range(steps):
+        acc.zero_()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        dq_atomic_floor(acc, w.causal)
+        e1.record(stream)
+        times.append((e0, e1))
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in times]))
+    nkt = (S + 127) // 128
+    nb = (S + 31) // 32
+    blocks = sum(nb - 4 * kt for kt in range(nkt)) if w.causal else nkt * nb
+    ops = B * H * blocks * 32 * hd
+    rec = {
+        "kind": "fp32 atomic adds of the atomic dQ design alone: one per dQ element per "
+                "(128-key workgroup, 32-query block) pair, no loads or matrix work",
+        "kernel": "dq_atomic_floor_kernel", "atomic_lane_ops": int(ops), "avg_ms": round(ms, 4),
+        "g_atomics_per_s": round(ops / (ms * 1e-3) / 1e9, 1), "counts_exact": ok,
+    }
+    if bwd_ms:
+        rec["fused_bwd_ms"] = round(bwd_ms, 4)
+        rec["floor_over_fused_bwd"] = round(ms / bwd_ms, 2)
+    return rec
 
 
 def causal_softmax(s, scale, causal):

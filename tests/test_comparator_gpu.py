@@ -69,3 +69,13 @@ def test_causal_softmax_kernel(dtype, S, causal):
     assert err <= (4e-3 if dtype == "bf16" else 1e-6)
     if causal:
         assert np.all(got[..., np.triu_indices(S, 1)[0], np.triu_indices(S, 1)[1]] == 0)
+
+
+@pytest.mark.parametrize("S,hd,causal", [(300, 64, True), (257, 32, False), (1024, 128, True)])
+def test_atomic_floor_counts(S, hd, causal):
+    say(f"atomic floor S={S} hd={hd} causal={causal}")
+    acc = torch.zeros((2, 3, S, hd), dtype=torch.float32, device="cuda")
+    comparator.dq_atomic_floor(acc, causal)
+    torch.cuda.synchronize()
+    exp = torch.from_numpy(comparator.dq_atomic_floor_expected(S, hd, causal)).cuda()
+    assert torch.equal(acc, exp.expand_as(acc))
