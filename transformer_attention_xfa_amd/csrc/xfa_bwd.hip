@@ -23,12 +23,6 @@
 // in exchange there are no atomics, no cross-workgroup ordering and no
 // workspace, and dQ is bitwise reproducible.
 //
-// bf16 without dropout uses the eight-wave key workgroup (key2_role): the two
-// waves of a SIMD share 32 keys and take alternate query blocks, in opposite
-// phases, so one wave's exponentials overlap the other's contractions; the
-// fp32 and dropout instantiations use the one-wave-per-SIMD key workgroup
-// (key_role), whose single wave interleaves its own work by hand.
-//
 // Pipeline.  The streamed 32-row blocks (Q, dO, L, D for a key workgroup;
 // K, V for a query workgroup) rotate through four LDS buffers filled by DMA
 // (buffer loads that write LDS, xfa_stage.h), so no registers hold staged
@@ -664,264 +658,6 @@ __device__ __forceinline__ void query_role(const BwdParams<T>& p, int bh, int qq
   }
 }
 
-// ------------------------------------------- key workgroups, two waves per SIMD
-// Eight waves per workgroup of 128 keys: wave w holds key group g = w % 4 (32
-// keys) and query-block parity r = w / 4, so the two waves of a key group
-// (which the hardware places on one SIMD) share its keys and take alternate
-// 32-query blocks, each with its own dK, dV partials; the partials are
-// summed through LDS at the end.  With K in registers and V read from an LDS
-// image of the workgroup's keys, a wave fits in half the register file, so a
-// SIMD interleaves two waves' contractions and vector work instead of one.
-template <int HD>
-struct Key2Cfg {
-  static constexpr int NW = 8;
-  using KB = KeyBuf<bf16, HD, NW>;
-  using VD = Dma<bf16, HD, NW, 1, false>;
-  // ring slots: 0-1 hold parity-0 blocks (used in one iteration), 2-4 parity-1
-  // blocks (scored in one iteration, finished in the next)
-  static constexpr int NBUF = 5;
-  static constexpr size_t RING = NBUF * KB::BYTES;
-  static constexpr size_t VIMG = 4 * VD::TILE;            // V of the 128 keys, four 32-row images
-  static constexpr size_t LSCR = NW * 32 * 4;             // each wave's prescaled L strip
-  static constexpr size_t SMEM = RING + VIMG + LSCR;
-  static constexpr size_t PART = 4 * 2 * BlockGeo<bf16, HD, NW>::NDB * 16 * 64 * 4;  // partials of 4 waves
-  static_assert(PART <= RING + VIMG, "the partials reuse the ring and the V images");
-};
-
-template <int HD>
-__device__ __forceinline__ void key2_role(const BwdParams<bf16>& p, int bh, int kt, char* smem) {
-  using T = bf16;
-  using C = Key2Cfg<HD>;
-  using G = BlockGeo<T, HD, C::NW>;
-  using M = typename G::M;
-  using KB = typename C::KB;
-  constexpr int NB = G::NB, NDB = G::NDB, NC = G::NC;
-  constexpr uint32_t ROWB = G::ROWB;
-  constexpr int BKV = 128;
-
-  const int S = p.S;
-  const int l = lane(), h = l >> 5;
-  const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  const int g = w & 3, par = w >> 2;
-  const size_t hoff = (size_t)bh * S * HD;
-  const uint32_t head_bytes = (uint32_t)S * ROWB;
-  const rsrc_t rK = make_rsrc(p.K + hoff, head_bytes);
-
-  const int j0 = kt * BKV;
-  const int kj = j0 + 32 * g + (l & 31);         // this lane's key
-  const int nb = (S + NB - 1) / NB;
-  const int n0 = p.causal ? j0 / NB : 0;
-  const int nm = p.causal ? min(nb, n0 + BKV / NB) : n0;   // blocks [n0, nm) cross the diagonal
-  const int ni = (nb - n0 + 1) / 2;              // iterations of two blocks
-
-  // the slot of iteration i's block of parity r
-  auto slot = [&](int i, int r) { return r == 0 ? (unsigned)i % 2u : 2u + (unsigned)i % 3u; };
-  // (the slot's byte offset is made opaque, so the compiler forms each
-  // iteration's addresses from it instead of keeping every slot's addresses
-  // live across the loop)
-  auto buf = [&](int i, int r) {
-    uint32_t sb = slot(i, r) * (uint32_t)KB::BYTES;
-    asm volatile("" : "+s"(sb));
-    return KB(smem + sb);
-  };
-  const T* vimg = reinterpret_cast<const T*>(smem + C::RING + (size_t)g * C::VD::TILE);
-  float* lscr = reinterpret_cast<float*>(smem + C::RING + C::VIMG) + 32 * w;
-  const TileRead<T, HD, C::NW> rd;
-
-  // this lane's key row of K: B operand of S = Q.K^T
-  typename M::frag kf[NC];
-#pragma unroll
-  for (int c = 0; c < NC; ++c) kf[c] = bload16<bf16>(rK, (uint32_t)kj * ROWB + (c * M::KD + M::KW * h) * sizeof(T));
-#pragma unroll
-  for (int c = 0; c < NC; ++c) settle(kf[c]);
-
-  f32x16 dkacc[NDB], dvacc[NDB];
-#pragma unroll
-  for (int d = 0; d < NDB; ++d) {
-    dkacc[d] = zero16();
-    dvacc[d] = zero16();
-  }
-
-  using DM = typename KB::DM;
-  constexpr int NPW = DM::NPW;
-  DM dma;
-  dma.init({make_desc(p.Q + hoff, head_bytes), make_desc(p.dO + hoff, head_bytes)},
-           make_desc(p.Lse + (size_t)bh * S, (uint32_t)S * 4u), make_desc(p.Dl + (size_t)bh * S, (uint32_t)S * 4u));
-  const uint32_t smem0 = lds_addr(smem);
-  // iteration i consumes blocks n0 + 2i (parity 0) and n0 + 2i + 1 (parity 1)
-  auto fetch_iter = [&](int i) {
-    const int n = n0 + 2 * i;
-    dma.issue(smem0 + slot(i, 0) * (uint32_t)KB::BYTES, n * NB);
-    dma.issue(smem0 + slot(i, 1) * (uint32_t)KB::BYTES, (n + 1) * NB);
-  };
-  {
-    // V of the workgroup's 128 keys (rows past the sequence end read as zeros)
-    typename C::VD vd;
-    const u32x4s dV = make_desc(p.V + hoff, head_bytes);
-    vd.init({dV}, dV, dV);
-#pragma unroll
-    for (int gg = 0; gg < 4; ++gg) vd.issue(smem0 + (uint32_t)(C::RING + gg * C::VD::TILE), j0 + 32 * gg);
-  }
-  fetch_iter(0);
-  wait_vm<0>();
-  __syncthreads();
-
-  // One 32-query block: S = Q.K^T and dP = dO.V^T with the lane owning a key
-  // (scores), then p = 2^(s c - L log2 e), dS = p (dp - D), dV^T += dO^T.P,
-  // dK^T += Q^T.dS (finish).  Parity-0 waves score and finish each block in
-  // one iteration; parity-1 waves finish the block they scored in the previous
-  // iteration and then score the next, carrying S and dP across the barrier,
-  // so the two waves of a SIMD are in opposite phases: one forms contractions
-  // while the other evaluates exponentials.
-  constexpr int PDS = 1, PDG = 1;                 // operand lookahead (contraction steps)
-  auto scores = [&](KB b, f32x16& s, f32x16& dp) {
-    s = zero16();
-    dp = zero16();
-    // operands read PDS steps ahead (the fences keep the compiler from
-    // hoisting every read, which would not fit)
-    typename M::frag qa[PDS + 1], oa[PDS + 1], va[PDS + 1];
-    auto read_sc = [&](int c) {
-      qa[c % (PDS + 1)] = rd.nat(b.q, c);
-      oa[c % (PDS + 1)] = rd.nat(b.dO, c);
-      va[c % (PDS + 1)] = rd.nat(vimg, c);
-    };
-#pragma unroll
-    for (int c = 0; c < PDS; ++c) read_sc(c);
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      __builtin_amdgcn_sched_barrier(0);
-      if (c + PDS < NC) read_sc(c + PDS);
-      s = M::mma(qa[c % (PDS + 1)], kf[c], s);
-      dp = M::mma(oa[c % (PDS + 1)], va[c % (PDS + 1)], dp);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  // P and dS of a block as the bf16 fragments of its two 16-deep gradient steps
-  struct Frags { typename M::frag p[2], ds[2]; };
-  auto softmax = [&](auto masked, KB b, int n, const f32x16& s, const f32x16& dp, Frags& f) {
-    if (l < 32) lscr[l] = -b.L[l] * kLog2e;      // this wave's copy of -L log2 e
-    const int lo = kj - (n * NB + 4 * h);         // masked: query row rel sees key kj iff rel >= lo
-#pragma unroll
-    for (int gg = 0; gg < 4; ++gg) {
-      const f32x4 L4 = *reinterpret_cast<const f32x4*>(lscr + 8 * gg + 4 * h);
-      const f32x4 D4 = *reinterpret_cast<const f32x4*>(b.D + 8 * gg + 4 * h);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int v = 4 * gg + e;
-        float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[v], p.c_log2, L4[e]));
-        float dv = pv * (dp[v] - D4[e]);
-        if constexpr (decltype(masked)::value) {
-          const bool keep = 8 * (v >> 2) + (v & 3) >= lo;
-          pv = keep ? pv : 0.f;
-          dv = keep ? dv : 0.f;
-        }
-        f.p[v >> 3][v & 7] = (bf16)pv;
-        f.ds[v >> 3][v & 7] = (bf16)dv;
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  auto grads = [&](KB b, const Frags& f) {
-    typename M::frag ta[PDG + 1], tb[PDG + 1];
-    auto read_tr = [&](int st) {                  // gradient step st = u * NDB + d
-      ta[st % (PDG + 1)] = rd.tr(b.dO, st / NDB, st % NDB);
-      tb[st % (PDG + 1)] = rd.tr(b.q, st / NDB, st % NDB);
-    };
-#pragma unroll
-    for (int st = 0; st < PDG && st < 2 * NDB; ++st) read_tr(st);
-#pragma unroll
-    for (int st = 0; st < 2 * NDB; ++st) {
-      const int u = st / NDB, d = st % NDB;
-      __builtin_amdgcn_sched_barrier(0);
-      if (st + PDG < 2 * NDB) read_tr(st + PDG);
-      dvacc[d] = M::mma(ta[st % (PDG + 1)], f.p[u], dvacc[d]);
-      dkacc[d] = M::mma(tb[st % (PDG + 1)], f.ds[u], dkacc[d]);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  auto end_iter = [&]() {
-    wait_vm<0>();                                // the next iteration's blocks landed
-    __syncthreads();
-  };
-
-  // iteration i: blocks n0 + 2i (parity 0) and n0 + 2i + 1 (parity 1); this
-  // wave's blocks below nm cross the diagonal (separate loops keep the
-  // accumulators in place)
-  const int im = (nm - n0 - par + 1) / 2;        // this wave's masked iterations
-  f32x16 s, dp;
-  Frags f;
-  if (par == 0) {
-    auto iter = [&](auto masked, int i) {
-      fetch_iter(i + 1);                         // into slots freed at the last barrier
-      const KB b = buf(i, 0);
-      scores(b, s, dp);
-      softmax(masked, b, n0 + 2 * i, s, dp, f);
-      grads(b, f);
-      end_iter();
-    };
-    int i = 0;
-    for (; i < im; ++i) iter(std::true_type{}, i);
-    for (; i < ni; ++i) iter(std::false_type{}, i);
-  } else {
-    // iteration i runs the gradient contractions of the block of iteration
-    // i - 1 (its P, dS fragments carried across the barrier), then scores
-    // and exponentials of its own
-    auto iter = [&](auto masked, int i) {
-      fetch_iter(i + 1);
-      if (i > 0) grads(buf(i - 1, 1), f);
-      const KB b = buf(i, 1);
-      scores(b, s, dp);
-      softmax(masked, b, n0 + 2 * i + 1, s, dp, f);
-      end_iter();
-    };
-    int i = 0;
-    for (; i < im; ++i) iter(std::true_type{}, i);
-    for (; i < ni; ++i) iter(std::false_type{}, i);
-    grads(buf(ni - 1, 1), f);
-  }
-  __syncthreads();                               // every wave is done with the ring and V
-
-  // sum the two parities' partials: parity 1 leaves them in LDS (over the
-  // ring and the V images, all reads of which ended at the last barrier)
-  f32x4* part = reinterpret_cast<f32x4*>(smem) + (size_t)g * (2 * NDB * 4 * 64) + l;
-  if (par == 1) {
-#pragma unroll
-    for (int d = 0; d < NDB; ++d)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        part[((2 * d) * 4 + e) * 64] = f32x4{dkacc[d][4 * e], dkacc[d][4 * e + 1], dkacc[d][4 * e + 2], dkacc[d][4 * e + 3]};
-        part[((2 * d + 1) * 4 + e) * 64] = f32x4{dvacc[d][4 * e], dvacc[d][4 * e + 1], dvacc[d][4 * e + 2], dvacc[d][4 * e + 3]};
-      }
-  }
-  __syncthreads();
-  if (par == 1) return;
-#pragma unroll
-  for (int d = 0; d < NDB; ++d)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const f32x4 a = part[((2 * d) * 4 + e) * 64], b = part[((2 * d + 1) * 4 + e) * 64];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        dkacc[d][4 * e + k] += a[k];
-        dvacc[d][4 * e + k] += b[k];
-      }
-    }
-  const rsrc_t rdK = make_rsrc(p.dK + hoff, head_bytes);
-  const rsrc_t rdV = make_rsrc(p.dV + hoff, head_bytes);
-  const uint32_t krow = (uint32_t)kj * ROWB;   // keys past the end are dropped
-#pragma unroll
-  for (int d = 0; d < NDB; ++d) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int dd = d * 32 + 8 * e + 4 * h;
-      if (G::HDP == HD || dd < HD) {
-        store4<T>(rdK, krow + dd * sizeof(T), dkacc[d], e, p.scale);
-        store4<T>(rdV, krow + dd * sizeof(T), dvacc[d], e, 1.f);
-      }
-    }
-  }
-}
-
 // ------------------------------------------------------------------ kernel
 template <typename T, int HD>
 struct BwdCfg {
@@ -942,15 +678,6 @@ __global__ __launch_bounds__((BwdCfg<T, HD>::NW * 64), 1) void bwd_key_kernel(Bw
   const int lid = xcd_logical(blockIdx.x, nwg);
   const int bh = lid / nkt;
   key_role<T, HD, C::NW, DROP>(p, bh, lid - bh * nkt, smem);
-}
-
-// bf16 without dropout: eight waves per 128 keys, two per SIMD
-template <int HD>
-__global__ __launch_bounds__(512, 1) void bwd_key2_kernel(BwdParams<bf16> p, int nkt, int nwg) {
-  __shared__ __attribute__((aligned(16))) char smem[Key2Cfg<HD>::SMEM];
-  const int lid = xcd_logical(blockIdx.x, nwg);
-  const int bh = lid / nkt;
-  key2_role<HD>(p, bh, lid - bh * nkt, smem);
 }
 
 // (with dropout the generator's 64-bit arithmetic needs more than half the
@@ -977,8 +704,6 @@ static hipError_t launch_bwd_t(const BwdArgs& a) {
   const int nk = (int)(a.BH * nkt), nq = (int)(a.BH * nqq);
   if (a.drop.thresh)
     hipLaunchKernelGGL((bwd_key_kernel<T, HD, true>), dim3(nk), dim3(C::NW * 64), 0, a.stream, p, nkt, nk);
-  else if constexpr (sizeof(T) == 2)
-    hipLaunchKernelGGL((bwd_key2_kernel<HD>), dim3(nk), dim3(512), 0, a.stream, p, nkt, nk);
   else
     hipLaunchKernelGGL((bwd_key_kernel<T, HD, false>), dim3(nk), dim3(C::NW * 64), 0, a.stream, p, nkt, nk);
   hipError_t e = hipGetLastError();
