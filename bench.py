@@ -75,6 +75,54 @@ def measured_traffic(phase: str, w) -> float | None:
     return float(rec["hbm_bytes_per_launch"])
 
 
+PHASE_KERNELS = {"fwd": ("fwd_kernel",), "pre": ("bwd_pre_kernel",), "bwd": ("bwd_key_kernel", "bwd_query_kernel")}
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+COPY_BYTES = 2 ** 30     # what --copy-calibration copies per dispatch
+
+
+def _counter_means(path: str) -> dict:
+    """Mean Counter_Value per kernel (by the kernel's unqualified name) of a
+    rocprofv3 --pmc csv with one counter."""
+    import csv
+
+    acc = {}
+    with open(path, newline="") as f:
+        for row in csv.DictReader(f):
+            name = row["Kernel_Name"]
+            for base in [k for ks in PHASE_KERNELS.values() for k in ks] + [COPY_KERNEL]:
+                if base in name:
+                    acc.setdefault(base, []).append(float(row["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in acc.items()}
+
+
+def ingest_pmc(fetch_csv: str, write_csv: str, copy_fetch_csv: str, copy_write_csv: str, workload: str) -> dict:
+    """profiles/traffic.json from two counter runs of bench.py (FETCH_SIZE,
+    WRITE_SIZE) and the same two counters over --copy-calibration: each
+    counter is scaled by the bytes a 1 GiB copy moves per unit of it, per
+    launch, and stamped with the digest of the sources it was taken on."""
+    fetch, write = _counter_means(fetch_csv), _counter_means(write_csv)
+    cf, cw = _counter_means(copy_fetch_csv)[COPY_KERNEL], _counter_means(copy_write_csv)[COPY_KERNEL]
+    ff, fw = COPY_BYTES / (cf * 1024), COPY_BYTES / (cw * 1024)
+    out = {"_note": "HBM bytes per launch on the named workload, from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE "
+                    "(KiB per dispatch, mean over the dispatches of each kernel), scaled by what a 1 GiB "
+                    "device-to-device copy (bench.py --copy-calibration) reads and writes on the same counters; "
+                    "the bwd phase is its two kernels' sum.  Written by bench.py --ingest-pmc.",
+           "calibration": {"copy_bytes": COPY_BYTES, "fetch_kib": cf, "write_kib": cw,
+                           "fetch_factor": round(ff, 4), "write_factor": round(fw, 4)}}
+    for phase, kernels in PHASE_KERNELS.items():
+        if not all(k in fetch and k in write for k in kernels):
+            continue
+        rd = sum(fetch[k] for k in kernels) * 1024 * ff
+        wr = sum(write[k] for k in kernels) * 1024 * fw
+        out[phase] = {"kernels": {k: {"fetch_kib": fetch[k], "write_kib": write[k]} for k in kernels},
+                      "workload": workload, "source_digest": source_digest(phase),
+                      "read_bytes": round(rd), "write_bytes": round(wr), "hbm_bytes_per_launch": round(rd + wr)}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    return out
+
+
 def gpu_bench(x, steps: int, warmup: int, dropout_p: float = 0.0, seed: int = 0x5EED):
     import torch
 
@@ -330,6 +378,12 @@ def main(argv=None):
     ap.add_argument("--dq-atomic-floor", action="store_true",
                     help="also time the fp32 atomic traffic alone that summing dQ across key workgroups "
                          "would need (the alternative to the separate dQ kernel)")
+    ap.add_argument("--ingest-pmc", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="write profiles/traffic.json from rocprofv3 --pmc csv files of bench.py (FETCH_SIZE, "
+                         "WRITE_SIZE, on --workload) and of --copy-calibration (same counters), then exit")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run three 1 GiB device-to-device copies (the reference kernel that scales the "
+                         "FETCH_SIZE / WRITE_SIZE counters to bytes) and exit")
     ap.add_argument("--dropout", type=float, default=0.0, metavar="P",
                     help="also time the step with dropout probability P on the attention probabilities")
     args = ap.parse_args(argv)
@@ -342,6 +396,18 @@ def main(argv=None):
               file=sys.stderr)
         return 2
 
+    if args.ingest_pmc:
+        print(json.dumps(ingest_pmc(*args.ingest_pmc, workload=args.workload)), flush=True)
+        return 0
+    if args.copy_calibration:
+        import torch
+        a = torch.ones(2 ** 28, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": a.numel() * 4, "copies": 3}), flush=True)
+        return 0
     w = workloads.BY_NAME[args.workload]
     x = workloads.make_inputs(w)
     # the oracle's worker pool runs before this process touches the GPU

@@ -12,7 +12,7 @@
 namespace xfa {
 
 constexpr int kPreThreads = 256;
-constexpr int kPreUnroll = 4;
+constexpr int kPreUnroll = 2;
 
 template <typename T, int HD>
 __global__ __launch_bounds__(kPreThreads) void bwd_pre_kernel(
