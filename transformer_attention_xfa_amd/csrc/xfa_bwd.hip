@@ -26,18 +26,22 @@
 // Pipeline.  The streamed 32-row blocks (Q, dO, L, D for a key workgroup;
 // K, V for a query workgroup) rotate through four LDS buffers filled by DMA
 // (buffer loads that write LDS, xfa_stage.h), so no registers hold staged
-// data: block m+3 is fetched at the start of iteration m into the buffer
-// block m-1 used, a block has more than an iteration to land, and one
-// `s_waitcnt vmcnt` plus one workgroup barrier end each iteration.  In a key
-// workgroup (one wave per SIMD), bf16 iteration n forms the two score
+// data: block m+3 is fetched during iteration m into the buffer block m-1
+// used, a block has more than an iteration to land, and one `s_waitcnt
+// vmcnt` plus one workgroup barrier end each iteration.  A wave stalls on
+// the issue of each 1 KiB strip of a fetch, so the strips go out one at a
+// time between contractions, which keep the matrix core busy meanwhile.  In
+// a key workgroup (one wave per SIMD), bf16 iteration n forms the two score
 // contractions of block n+1 interleaved with the exponentials and dS of
 // block n, then block n's u = 0 gradient contractions; its u = 1 gradient
 // contractions run at the start of iteration n+1 from operands carried in
-// registers across the barrier.  The score contractions of n+1 do not depend
-// on block n's exponentials, so the matrix cores have work while the vector
-// units evaluate them.  A query workgroup runs two waves per SIMD and
-// interleaves the same way (scores of block n+1 between the exponentials and
-// transposed K reads of block n, then block n's dQ contractions).
+// registers across the barrier, with that iteration's fetch spread over
+// them.  The score contractions of n+1 do not depend on block n's
+// exponentials, so the matrix cores have work while the vector units
+// evaluate them.  A query workgroup runs two waves per SIMD and interleaves
+// the same way (scores of block n+1 between the exponentials and transposed
+// K reads of block n, then block n's dQ contractions, with the fetch spread
+// over those).
 //
 // The operands whose contraction index runs along block rows (dO^T and Q^T
 // for the key workgroups, K^T for the query workgroups) are read from the
@@ -255,6 +259,24 @@ __device__ __forceinline__ void key_role(const BwdParams<T>& p, int bh, int kt, 
       dkacc[d] = M::mma(ctb[d], csf, dkacc[d]);
     }
   };
+  // The same contractions with block nf's fetch spread between them: one
+  // strip after each contraction, so the wave's stall on each strip's issue
+  // overlaps a contraction instead of idling the matrix core.
+  auto carried_fetch = [&](int nf) {
+    const uint32_t fb = smem0 + (uint32_t)((unsigned)nf % NBUF) * KB::BYTES;
+#pragma unroll
+    for (int d = 0; d < NDB; ++d) {
+      __builtin_amdgcn_sched_barrier(0);
+      dvacc[d] = M::mma(cta[d], cpf, dvacc[d]);
+      if (2 * d < NPW) dma.issue_one(fb, nf * NB, 2 * d);
+      __builtin_amdgcn_sched_barrier(0);
+      dkacc[d] = M::mma(ctb[d], csf, dkacc[d]);
+      if (2 * d + 1 < NPW) dma.issue_one(fb, nf * NB, 2 * d + 1);
+    }
+#pragma unroll
+    for (int t = 2 * NDB; t < NPW; ++t) dma.issue_one(fb, nf * NB, t);
+    __builtin_amdgcn_sched_barrier(0);
+  };
   // bf16 iteration with the work interleaved by hand (sched_barrier fences
   // keep the order): the score contractions of block n+1 alternate with the
   // exponentials and dS of block n and the reads of block n's gradient
@@ -263,7 +285,6 @@ __device__ __forceinline__ void key_role(const BwdParams<T>& p, int bh, int kt, 
     if constexpr (BF) {
       static_assert(NU == 2, "bf16 contraction steps are 16 deep");
       const float lx = prescale_read(n + 1);
-      fetch(n + NBUF - 1);       // into the buffer of block n-1, finished before the last barrier
       KB bn = buf(n + 1), bc = buf(n);
       f32x16& sn = pipe.next(par).s;
       f32x16& dn = pipe.next(par).dp;
@@ -343,7 +364,11 @@ __device__ __forceinline__ void key_role(const BwdParams<T>& p, int bh, int kt, 
         if (ld_step(g) < 0) read_ld(g);
 #pragma unroll
       for (int c = 0; c < PD && c < NC; ++c) read_sc(c);
-      carried();                 // block n-1, u = 1
+      // the first reads go out ahead of the carried contractions (block
+      // n-1, u = 1), which cover their latency; block n+3 is fetched into
+      // the buffer of block n-1, finished before the last barrier
+      __builtin_amdgcn_sched_barrier(0);
+      carried_fetch(n + NBUF - 1);
       sn = zero16();
       dn = zero16();
 #pragma unroll
@@ -571,7 +596,9 @@ __device__ __forceinline__ void query_role(const BwdParams<T>& p, int bh, int qq
     sdp(0, sa, pa);
     Pipe pipe(sa, pa, sb, pb);
     auto body = [&](auto masked, auto par, int n) {
-      fetch(n + NBUF - 1);       // into the buffer of block n-1, finished before the last barrier
+      // block n+3 goes into the buffer of block n-1, finished before the
+      // last barrier; its strips are issued between the dQ contractions
+      const uint32_t fb = smem0 + (uint32_t)((unsigned)(n + NBUF - 1) % NBUF) * QB::BYTES;
       QB bn = buf(n + 1), bc = buf(n);
       f32x16& sn = pipe.next(par).s;
       f32x16& dn = pipe.next(par).dp;
@@ -612,9 +639,12 @@ __device__ __forceinline__ void query_role(const BwdParams<T>& p, int bh, int qq
       for (int g = 0; g < NG; ++g) {
         __builtin_amdgcn_sched_barrier(0);
         dqacc[g % NDB] = M::mma(ta[g], sf[g / NDB], dqacc[g % NDB]);
+        if (g < NPW) dma.issue_one(fb, (n + NBUF - 1) * NB, g);
         if (g + NGA < NG) read_tr(g + NGA);
       }
       __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int t = NG; t < NPW; ++t) dma.issue_one(fb, (n + NBUF - 1) * NB, t);
       wait_vm<(NBUF - 3) * NPW>();   // block n+2 landed, later ones in flight
       __syncthreads();
     };

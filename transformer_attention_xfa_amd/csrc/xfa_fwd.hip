@@ -17,7 +17,9 @@
 // m + 3 is fetched while block m is processed, and one wait plus one barrier
 // end each iteration.  bf16 iterations interleave the score contractions of
 // block n+1 with the exponentials of block n and the reads of block n's V^T
-// operands, then run block n's P.V contractions.
+// operands, then run block n's P.V contractions with the strips of block
+// n+3's fetch issued between them (a wave stalls on each strip's issue, and
+// a contraction in flight covers that stall).
 //
 // The exponent is taken in base 2: with c = scale * log2(e) and a reference
 // maximum m (log2 units), p = 2^(x c - m) is one fused multiply-add and one
@@ -245,7 +247,9 @@ __global__ __launch_bounds__(NW * 64, (sizeof(T) == 2 ? 2 : 1)) void fwd_kernel(
       auto read_v = [&](int g) { va[g] = rd.tr(bc.v, g / NDB, g % NDB); };
 #pragma unroll
       for (int c = 0; c < PD && c < NC; ++c) read_k(c);
-      fetch(n + NBUF - 1);         // into the buffer of block n-1, finished before the last barrier
+      // block n+3 goes into the buffer of block n-1, finished before the
+      // last barrier; its strips are issued between the P.V contractions
+      const uint32_t fb = smem0 + (uint32_t)((unsigned)(n + NBUF - 1) % NBUF) * FB::BYTES;
       if constexpr (DROP) prepare(masked, n, s);
       else mask_only(masked, n, s);
       const uint64_t bg = block_g(n);
@@ -292,9 +296,12 @@ __global__ __launch_bounds__(NW * 64, (sizeof(T) == 2 ? 2 : 1)) void fwd_kernel(
       for (int g = 0; g < NG; ++g) {
         __builtin_amdgcn_sched_barrier(0);
         oacc[g % NDB] = M::mma(va[g], pf[g / NDB], oacc[g % NDB]);
+        if (g < NPW) dma.issue_one(fb, (n + NBUF - 1) * NB, g);
         if (g + NGA < NG) read_v(g + NGA);
       }
       __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int t = NG; t < NPW; ++t) dma.issue_one(fb, (n + NBUF - 1) * NB, t);
       wait_vm<(NBUF - 3) * NPW>();   // block n+2 landed, later ones in flight
       __syncthreads();
     };

@@ -234,16 +234,19 @@ struct Dma {
       rel[t] = r;
     }
   }
-  // Issue this wave's strips of block rows [row0, row0 + NB) into the image
-  // at LDS byte `base`.
+  // Issue strip t of this wave (t < NPW) of block rows [row0, row0 + NB)
+  // into the image at LDS byte `base`.  A wave's issue stalls while the
+  // load unit takes each strip, so kernels spread a block's strips between
+  // contractions instead of issuing them back to back.
+  __device__ inline void issue_one(uint32_t base, int row0, int t) const {
+    // an out-of-range slot (rel = 2^31) stays at or above 2^31 without
+    // wrapping: the entry points keep (S + 256) rows of fp32 below 2^31 bytes
+    dma16(desc[t], rel[t] + (uint32_t)row0 * step[t], base + dst[t]);
+  }
+  // All of this wave's strips of the block, back to back.
   __device__ inline void issue(uint32_t base, int row0) const {
 #pragma unroll
-    for (int t = 0; t < NPW; ++t) {
-      // an out-of-range slot (rel = 2^31) stays at or above 2^31 without
-      // wrapping: the entry points keep (S + 256) rows of fp32 below 2^31 bytes
-      const uint32_t off = rel[t] + (uint32_t)row0 * step[t];
-      dma16(desc[t], off, base + dst[t]);
-    }
+    for (int t = 0; t < NPW; ++t) issue_one(base, row0, t);
   }
 };
 
