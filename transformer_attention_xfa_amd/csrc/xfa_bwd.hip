@@ -333,8 +333,9 @@ __device__ __forceinline__ void key_role(const BwdParams<T>& p, int bh, int kt, 
       constexpr int EA = (SPLIT + NC - 1) / NC;          // elements per score step
       constexpr int EB = (16 - SPLIT + NDB - 1) / NDB;   // elements per u = 0 gradient step
       auto fin_step = [](int v) { return v < SPLIT ? v / EA : NC + (v - SPLIT) / EB; };
-      // row group g of L and D is read one step before its first element
-      auto ld_step = [&](int g) { return fin_step(4 * g) - 1; };
+      // row group g of L and D is read two steps before its first element
+      // (one step ahead left the exponentials waiting on the read: +1 %)
+      auto ld_step = [&](int g) { return fin_step(4 * g) - 2; };
       auto softmax = [&](int v) {
         const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[v], p.c_log2, L4[v >> 2][v & 3]));
         const float m = mask(bg, v);
