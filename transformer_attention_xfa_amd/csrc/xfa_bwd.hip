@@ -701,14 +701,16 @@ struct BwdCfg {
 // Two launches on the caller's stream.  Key workgroups (heaviest first: the
 // earliest keys see the most queries) need the whole register file, one wave
 // per SIMD; query workgroups (heaviest first: the last queries see the most
-// keys) fit two waves per SIMD for bf16.  A head's workgroups stay on one XCD.
+// keys) fit two waves per SIMD for bf16.  Both dispatch heads in groups of
+// four with the group's tiles interleaved (group_order), a group's
+// workgroups on one XCD.
 template <typename T, int HD, bool DROP>
-__global__ __launch_bounds__((BwdCfg<T, HD>::NW * 64), 1) void bwd_key_kernel(BwdParams<T> p, int nkt, int nwg) {
+__global__ __launch_bounds__((BwdCfg<T, HD>::NW * 64), 1) void bwd_key_kernel(BwdParams<T> p, int nkt, int nwg, int BH) {
   using C = BwdCfg<T, HD>;
   __shared__ __attribute__((aligned(16))) char smem[C::KEY_BYTES];
-  const int lid = xcd_logical(blockIdx.x, nwg);
-  const int bh = lid / nkt;
-  key_role<T, HD, C::NW, DROP>(p, bh, lid - bh * nkt, smem);
+  int bh, rank;
+  group_order<4>(xcd_logical(blockIdx.x, nwg), nkt, BH, bh, rank);
+  key_role<T, HD, C::NW, DROP>(p, bh, rank, smem);
 }
 
 // (with dropout the generator's 64-bit arithmetic needs more than half the
@@ -719,7 +721,7 @@ __global__ __launch_bounds__((BwdCfg<T, HD>::NW * 64), (sizeof(T) == 2 && !DROP 
   using C = BwdCfg<T, HD>;
   __shared__ __attribute__((aligned(16))) char smem[C::QUERY_BYTES];
   int bh, rank;
-  pair_order(xcd_logical(blockIdx.x, nwg), nqq, BH, bh, rank);
+  group_order<4>(xcd_logical(blockIdx.x, nwg), nqq, BH, bh, rank);
   query_role<T, HD, C::NW, DROP>(p, bh, nqq - 1 - rank, smem);
 }
 
@@ -734,9 +736,9 @@ static hipError_t launch_bwd_t(const BwdArgs& a) {
                  (T*)a.dq, (T*)a.dk, (T*)a.dv, (int)a.S, a.scale, a.scale * kLog2e, a.causal, a.drop};
   const int nk = (int)(a.BH * nkt), nq = (int)(a.BH * nqq);
   if (a.drop.thresh)
-    hipLaunchKernelGGL((bwd_key_kernel<T, HD, true>), dim3(nk), dim3(C::NW * 64), 0, a.stream, p, nkt, nk);
+    hipLaunchKernelGGL((bwd_key_kernel<T, HD, true>), dim3(nk), dim3(C::NW * 64), 0, a.stream, p, nkt, nk, (int)a.BH);
   else
-    hipLaunchKernelGGL((bwd_key_kernel<T, HD, false>), dim3(nk), dim3(C::NW * 64), 0, a.stream, p, nkt, nk);
+    hipLaunchKernelGGL((bwd_key_kernel<T, HD, false>), dim3(nk), dim3(C::NW * 64), 0, a.stream, p, nkt, nk, (int)a.BH);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.drop.thresh)

@@ -187,25 +187,26 @@ __device__ inline int xcd_logical(int bid, int n) {
   return x * q + (x < r ? x : r) + slot;
 }
 
-// Logical order of the query-tile workgroups (forward, backward query role):
-// heads are taken in pairs and the tiles of the two heads interleaved,
-// heaviest first (rank 0 = the tile with the most causal work); an odd last
-// head runs alone.  Two workgroups share each CU, so an XCD runs two heads at
-// once; dispatching each head's tiles heaviest first on its own would leave
-// the light tiles of both heads finishing together and the next pair's heavy
-// tiles starting late (a ~10 % tail in a greedy-dispatch model of one XCD),
-// while one longest-first list per pair keeps the slots level and still
-// confines the streamed K/V (or K/V/dO) to two heads per L2.
-__device__ inline void pair_order(int lid, int nt, int BH, int& bh, int& rank) {
-  const int pair = lid / (2 * nt);
-  const int r = lid - pair * 2 * nt;
-  if (2 * pair + 1 < BH) {
-    bh = 2 * pair + (r & 1);
-    rank = r >> 1;
-  } else {
-    bh = 2 * pair;
-    rank = r;
-  }
+// Logical order of the tile workgroups (forward, both backward roles): heads
+// are taken in groups of G and the tiles of the group's heads interleaved,
+// heaviest first (rank 0 = the tile with the most causal work); a short last
+// group takes the heads that remain.  Dispatching each head's tiles heaviest
+// first on its own leaves a head's light tiles finishing together and the
+// next head's heavy tiles starting late (a ~10 % tail in a greedy-dispatch
+// model of one XCD), while one longest-first list per group keeps the CUs
+// level and still confines the streamed blocks to G heads per L2.  Measured
+// on C4 (forward time; preprocess + backward time): two-head groups against
+// one head at a time, forward and query kernel about 4 % each, backward 1.4 %
+// more with the key kernel's tiles grouped too; four-head groups against two,
+// forward 2.0 %, backward 1.0 % (query kernel) and 0.7 % (key kernel); eight
+// or more heads, or three or six, made the key kernel slower.
+template <int G>
+__device__ inline void group_order(int lid, int nt, int BH, int& bh, int& rank) {
+  const int grp = lid / (G * nt);
+  const int r = lid - grp * G * nt;
+  const int nh = min(G, BH - G * grp);   // heads in this group (fewer in the last)
+  bh = G * grp + r % nh;
+  rank = r / nh;
 }
 
 }  // namespace xfa

@@ -69,9 +69,9 @@ __global__ __launch_bounds__(NW * 64, (sizeof(T) == 2 ? 2 : 1)) void fwd_kernel(
 
   const int l = lane(), h = l >> 5, w = threadIdx.x >> 6;
 
-  // heaviest query tiles first, two heads' tiles together per XCD
+  // heaviest query tiles first, four heads' tiles together per XCD
   int bh, rank;
-  pair_order(xcd_logical(blockIdx.x, nwg), nqt, BH, bh, rank);
+  group_order<4>(xcd_logical(blockIdx.x, nwg), nqt, BH, bh, rank);
   const int qt = nqt - 1 - rank;
 
   const size_t hoff = (size_t)bh * S * HD;
