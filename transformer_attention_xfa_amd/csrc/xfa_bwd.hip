@@ -701,15 +701,15 @@ struct BwdCfg {
 // Two launches on the caller's stream.  Key workgroups (heaviest first: the
 // earliest keys see the most queries) need the whole register file, one wave
 // per SIMD; query workgroups (heaviest first: the last queries see the most
-// keys) fit two waves per SIMD for bf16.  Both dispatch heads in groups of
-// four with the group's tiles interleaved (group_order), a group's
+// keys) fit two waves per SIMD for bf16.  Both dispatch heads in groups
+// (head_group) with the group's tiles interleaved (group_order), a group's
 // workgroups on one XCD.
 template <typename T, int HD, bool DROP>
-__global__ __launch_bounds__((BwdCfg<T, HD>::NW * 64), 1) void bwd_key_kernel(BwdParams<T> p, int nkt, int nwg, int BH) {
+__global__ __launch_bounds__((BwdCfg<T, HD>::NW * 64), 1) void bwd_key_kernel(BwdParams<T> p, int nkt, int nwg, int BH, int hg) {
   using C = BwdCfg<T, HD>;
   __shared__ __attribute__((aligned(16))) char smem[C::KEY_BYTES];
   int bh, rank;
-  group_order<4>(xcd_logical(blockIdx.x, nwg), nkt, BH, bh, rank);
+  group_order(xcd_logical(blockIdx.x, nwg), nkt, BH, hg, bh, rank);
   key_role<T, HD, C::NW, DROP>(p, bh, rank, smem);
 }
 
@@ -717,11 +717,11 @@ __global__ __launch_bounds__((BwdCfg<T, HD>::NW * 64), 1) void bwd_key_kernel(Bw
 // register file: one workgroup per CU)
 template <typename T, int HD, bool DROP>
 __global__ __launch_bounds__((BwdCfg<T, HD>::NW * 64), (sizeof(T) == 2 && !DROP ? 2 : 1)) void bwd_query_kernel(
-    BwdParams<T> p, int nqq, int nwg, int BH) {
+    BwdParams<T> p, int nqq, int nwg, int BH, int hg) {
   using C = BwdCfg<T, HD>;
   __shared__ __attribute__((aligned(16))) char smem[C::QUERY_BYTES];
   int bh, rank;
-  group_order<4>(xcd_logical(blockIdx.x, nwg), nqq, BH, bh, rank);
+  group_order(xcd_logical(blockIdx.x, nwg), nqq, BH, hg, bh, rank);
   query_role<T, HD, C::NW, DROP>(p, bh, nqq - 1 - rank, smem);
 }
 
@@ -736,15 +736,15 @@ static hipError_t launch_bwd_t(const BwdArgs& a) {
                  (T*)a.dq, (T*)a.dk, (T*)a.dv, (int)a.S, a.scale, a.scale * kLog2e, a.causal, a.drop};
   const int nk = (int)(a.BH * nkt), nq = (int)(a.BH * nqq);
   if (a.drop.thresh)
-    hipLaunchKernelGGL((bwd_key_kernel<T, HD, true>), dim3(nk), dim3(C::NW * 64), 0, a.stream, p, nkt, nk, (int)a.BH);
+    hipLaunchKernelGGL((bwd_key_kernel<T, HD, true>), dim3(nk), dim3(C::NW * 64), 0, a.stream, p, nkt, nk, (int)a.BH, head_group(nkt));
   else
-    hipLaunchKernelGGL((bwd_key_kernel<T, HD, false>), dim3(nk), dim3(C::NW * 64), 0, a.stream, p, nkt, nk, (int)a.BH);
+    hipLaunchKernelGGL((bwd_key_kernel<T, HD, false>), dim3(nk), dim3(C::NW * 64), 0, a.stream, p, nkt, nk, (int)a.BH, head_group(nkt));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.drop.thresh)
-    hipLaunchKernelGGL((bwd_query_kernel<T, HD, true>), dim3(nq), dim3(C::NW * 64), 0, a.stream, p, nqq, nq, (int)a.BH);
+    hipLaunchKernelGGL((bwd_query_kernel<T, HD, true>), dim3(nq), dim3(C::NW * 64), 0, a.stream, p, nqq, nq, (int)a.BH, head_group(nqq));
   else
-    hipLaunchKernelGGL((bwd_query_kernel<T, HD, false>), dim3(nq), dim3(C::NW * 64), 0, a.stream, p, nqq, nq, (int)a.BH);
+    hipLaunchKernelGGL((bwd_query_kernel<T, HD, false>), dim3(nq), dim3(C::NW * 64), 0, a.stream, p, nqq, nq, (int)a.BH, head_group(nqq));
   return hipGetLastError();
 }
 

@@ -200,13 +200,20 @@ __device__ inline int xcd_logical(int bid, int n) {
 // more with the key kernel's tiles grouped too; four-head groups against two,
 // forward 2.0 %, backward 1.0 % (query kernel) and 0.7 % (key kernel); eight
 // or more heads, or three or six, made the key kernel slower.
-template <int G>
-__device__ inline void group_order(int lid, int nt, int BH, int& bh, int& rank) {
+__device__ inline void group_order(int lid, int nt, int BH, int G, int& bh, int& rank) {
   const int grp = lid / (G * nt);
   const int r = lid - grp * G * nt;
   const int nh = min(G, BH - G * grp);   // heads in this group (fewer in the last)
   bh = G * grp + r % nh;
   rank = r / nh;
+}
+// Heads per group for nt tiles per head: up to kGroupTiles tiles per group,
+// at most four heads (C4, 32 tiles per head: four; S = 16384, 128 tiles per
+// head: two, which measured 0.4-0.9 % faster than one or four there).
+constexpr int kGroupTiles = 256;
+inline int head_group(int64_t nt) {
+  const int64_t g = kGroupTiles / (nt > 0 ? nt : 1);
+  return (int)(g < 1 ? 1 : (g > 4 ? 4 : g));
 }
 
 }  // namespace xfa

@@ -55,7 +55,7 @@ struct FwdBuf {
 template <typename T, int HD, int NW, bool DROP>
 __global__ __launch_bounds__(NW * 64, (sizeof(T) == 2 ? 2 : 1)) void fwd_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, T* __restrict__ O,
-    float* __restrict__ Lse, int S, float c_log2, int causal, int nqt, int nwg, int BH, DropArgs drop) {
+    float* __restrict__ Lse, int S, float c_log2, int causal, int nqt, int nwg, int BH, int hg, DropArgs drop) {
   using G = BlockGeo<T, HD, NW>;
   using M = typename G::M;
   using FB = FwdBuf<T, HD, NW>;
@@ -69,9 +69,9 @@ __global__ __launch_bounds__(NW * 64, (sizeof(T) == 2 ? 2 : 1)) void fwd_kernel(
 
   const int l = lane(), h = l >> 5, w = threadIdx.x >> 6;
 
-  // heaviest query tiles first, four heads' tiles together per XCD
+  // heaviest query tiles first, hg heads' tiles together per XCD
   int bh, rank;
-  group_order<4>(xcd_logical(blockIdx.x, nwg), nqt, BH, bh, rank);
+  group_order(xcd_logical(blockIdx.x, nwg), nqt, BH, hg, bh, rank);
   const int qt = nqt - 1 - rank;
 
   const size_t hoff = (size_t)bh * S * HD;
@@ -361,11 +361,11 @@ static hipError_t launch_fwd_t(const FwdArgs& a) {
   if (a.drop.thresh)
     hipLaunchKernelGGL((fwd_kernel<T, HD, NW, true>), dim3(nwg), dim3(NW * 64), 0, a.stream,
                        (const T*)a.q, (const T*)a.k, (const T*)a.v, (T*)a.out, a.lse, (int)a.S,
-                       a.scale * kLog2e, a.causal, nqt, nwg, (int)a.BH, a.drop);
+                       a.scale * kLog2e, a.causal, nqt, nwg, (int)a.BH, head_group(nqt), a.drop);
   else
     hipLaunchKernelGGL((fwd_kernel<T, HD, NW, false>), dim3(nwg), dim3(NW * 64), 0, a.stream,
                        (const T*)a.q, (const T*)a.k, (const T*)a.v, (T*)a.out, a.lse, (int)a.S,
-                       a.scale * kLog2e, a.causal, nqt, nwg, (int)a.BH, a.drop);
+                       a.scale * kLog2e, a.causal, nqt, nwg, (int)a.BH, head_group(nqt), a.drop);
   return hipGetLastError();
 }
 
