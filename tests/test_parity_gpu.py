@@ -277,3 +277,23 @@ def test_other_shapes_at_scale(dtype, B, H, S, hd, causal):
     for bh in (0, w.BH - 1):
         compare_head(x, g, bh, row_block=1024)
     check_invariants(x, g)
+
+
+# ------------------------------------- dispatch groups with a short last group
+# Every kernel dispatches its tiles in groups of heads (up to four; three when
+# a head has 66 tiles), the group's tiles interleaved; these head counts leave
+# a short last group, whose heads must map to their own tiles like the rest.
+@pytest.mark.parametrize("dtype,B,H,S,hd,causal", [
+    ("bf16", 1, 5, 700, 64, True),       # 4 + 1 heads
+    ("bf16", 3, 2, 1100, 128, True),     # 4 + 2
+    ("f32", 1, 7, 300, 32, False),       # 4 + 3
+    ("bf16", 1, 4, 8448, 64, True),      # 66 tiles per head: groups of 3, 3 + 1
+])
+def test_dispatch_group_remainders(dtype, B, H, S, hd, causal):
+    w = workloads.Workload(f"groups_{dtype}_b{B}h{H}_s{S}_hd{hd}_{'c' if causal else 'f'}", dtype, B, H, S, hd,
+                           seed=4000 + S + hd, causal=causal, do_std=1.0 if dtype == "f32" else 0.1)
+    x = workloads.make_inputs(w)
+    g = run_gpu(x)
+    for bh in (range(w.BH) if S <= 2048 else (0, w.BH - 1)):
+        compare_head(x, g, bh, row_block=1024)
+    check_invariants(x, g)
