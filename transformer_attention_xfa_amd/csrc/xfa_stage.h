@@ -11,20 +11,23 @@
 namespace xfa {
 
 // Geometry of a streamed block of NB = 32 rows of a [S][HD] tensor and of its
-// LDS image.  The image holds row r in P consecutive 16-byte slots starting
-// at slot r * P; the CPR data slots of the row start at slot r * P + rot(r)
-// and the other slots of the row are zero.
-//   fp32: P = HDP / 4 + 1 (one slot of padding), rot = 0: a row stride of 4
-//         (mod 64) dwords, which the fp32 reads take without bank conflicts.
-//   bf16: P = 20 for 256-byte rows, else 12, and rot(r) = (r / 4) mod 4.  The
-//         slot group (slot mod 16, four of the 64 banks) of row r's first
-//         data slot is then the same modulo 4 and distinct for the four rows
-//         of a transposed read, and distinct over any 16 consecutive rows, so
-//         both the natural 16-byte reads (16 rows at one column) and the
-//         transpose reads (4 rows x 64 bytes per 32 lanes) touch every bank
-//         once.  The rotation repeats every 16 rows and rot(r + 8) =
-//         rot(r) + 2 for r mod 16 < 8, so every read address is a per-lane
-//         base plus a compile-time offset.
+// LDS image.  The image holds block row r in the P consecutive 16-byte slots
+// starting at slot phys(r) * P: its CPR data slots first, then zeros.
+//   fp32: P = HDP / 4 + 1 (one slot of padding), phys(r) = r: a row stride of
+//         4 (mod 64) dwords, which the fp32 reads take without bank conflicts.
+//   bf16: P = HDP / 8 + 1 (odd), and phys swaps the two low 2-bit fields of
+//         the row index (r = 16a + 4b + c sits at 16a + 4c + b; the map is its
+//         own inverse).  A slot's group (slot mod 16, four of the 64 banks)
+//         is then distinct for the first slots of any 16 consecutive rows
+//         (P is odd), which the natural 16-byte reads (16 rows at one column)
+//         need, and the four rows 4b..4b+3 of a transposed read sit at
+//         physical rows 4c + b, whose first slots are four groups apart, so
+//         the transpose reads (4 rows x 64 bytes per 32 lanes) touch every
+//         bank once too.  Rows r + 8 (r mod 16 < 8) and r + 16 sit 2 and 16
+//         physical rows further on, so every read address is a per-lane base
+//         plus a compile-time offset.  With the one slot of padding a 32-row
+//         block of 256-byte rows is 544 slots, nine 1 KiB DMA strips (a
+//         layout of 20-slot rows that needed no permutation took ten).
 template <typename T, int HD, int NW>
 struct BlockGeo {
   using M = Mma<T>;
@@ -35,12 +38,13 @@ struct BlockGeo {
   static constexpr int NC = HD / M::KD;          // instructions along d
   static constexpr int NU = 32 / M::KD;          // instructions per 32-wide k block
   static constexpr int CPR = HD * (int)sizeof(T) / 16;   // 16-byte data slots per row
-  static constexpr int P = BF ? (HDP == 128 ? 20 : 12) : HDP / 4 + 1;   // slots per LDS row
+  static constexpr int P = BF ? HDP / 8 + 1 : HDP / 4 + 1;   // slots per LDS row
   static constexpr int LD = P * 16 / (int)sizeof(T);   // elements per LDS row
   static constexpr uint32_t ROWB = HD * sizeof(T);     // bytes per source row
   static_assert(HD % M::KD == 0 && HD * sizeof(T) % 16 == 0, "unsupported head dim");
-  static_assert(!BF || P >= HDP / 8 + 3, "rotated rows must fit their slots");
-  __device__ static constexpr int rot(int r) { return BF ? (r >> 2) & 3 : 0; }
+  static_assert(!BF || P % 2 == 1, "an odd row length spreads 16 rows over the banks");
+  // physical row of block row r (and block row of physical row r)
+  __host__ __device__ static constexpr int phys(int r) { return BF ? (r & ~15) | ((r & 3) << 2) | ((r >> 2) & 3) : r; }
 };
 
 // Operand reads from a block image (bf16: natural 16-byte reads and the LDS
@@ -56,11 +60,11 @@ struct TileRead {
     if constexpr (G::BF) {
       // natural: row l % 32, elements 8 h .. 8 h + 7 of each 16-wide k step
       const int r = l & 31;
-      off_nat = 16u * (uint32_t)(r * G::P + G::rot(r) + h);
+      off_nat = 16u * (uint32_t)(G::phys(r) * G::P + h);
       // transposed: rows 4 h + t / 4 (+8, +16 u), bytes 32 nb + 8 (t % 4) of a
       // 64-byte column block (t = lane % 16, nb = bit 4 of the lane)
       const int t = l & 15, nb = (l >> 4) & 1, k = 4 * h + (t >> 2);
-      off_tr = 16u * (uint32_t)(k * G::P + G::rot(k)) + 32u * nb + 8u * (t & 3);
+      off_tr = 16u * (uint32_t)(G::phys(k) * G::P) + 32u * nb + 8u * (t & 3);
     } else {
       off_nat = 4u * (uint32_t)((l & 31) * G::LD + h * M::KW);
       off_tr = 4u * (uint32_t)(4 * h * G::LD + (l & 31));
@@ -79,7 +83,7 @@ struct TileRead {
     const char* p = reinterpret_cast<const char*>(img) + off_tr;
     if constexpr (G::BF) {
       const char* p0 = p + 16 * (16 * u * G::P) + 64 * d;
-      const char* p1 = p0 + 16 * (8 * G::P) + 32;   // rows + 8: rotation + 2
+      const char* p1 = p0 + 16 * (2 * G::P);   // rows + 8: two physical rows on
       const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p0);
       const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p1);
       const bf16x4 fa = __builtin_bit_cast(bf16x4, a);
@@ -223,8 +227,8 @@ struct Dma {
         desc[t] = d;
         dst[t] = (uint32_t)ten * TILE + (uint32_t)i * 1024u;
         step[t] = G::ROWB;
-        const int s = 64 * i + l, row = s / G::P, ch = s % G::P - G::rot(row);
-        if (row < G::NB && ch >= 0 && ch < G::CPR) r = (uint32_t)row * G::ROWB + (uint32_t)ch * 16u;
+        const int s = 64 * i + l, pr = s / G::P, ch = s % G::P;
+        if (pr < G::NB && ch < G::CPR) r = (uint32_t)G::phys(pr) * G::ROWB + (uint32_t)ch * 16u;
       } else {
         desc[t] = (j == NTEN * NI) ? dl : dd;
         dst[t] = (uint32_t)NTEN * TILE + (uint32_t)(j - NTEN * NI) * 1024u;
