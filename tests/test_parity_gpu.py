@@ -249,6 +249,38 @@ def test_nondefault_stream_and_repeatability():
         compare_head(x, g1, bh)
 
 
+def test_concurrent_calls_on_two_streams():
+    # The entry points keep no state between calls: two problems enqueued on
+    # two streams at once, nothing ordering one against the other, give each
+    # the result it gives alone.
+    xs = [workloads.make_inputs(workloads.Workload("conc_bf16_s1100_hd128", "bf16", 1, 3, 1100, 128, seed=71, do_std=0.1)),
+          workloads.make_inputs(workloads.Workload("conc_f32_s700_hd64", "f32", 2, 1, 700, 64, seed=72,
+                                                   causal=False, do_std=1.0))]
+    alone = [run_gpu(x) for x in xs]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    live = []
+    torch.cuda.synchronize()
+    for x, s in zip(xs, streams):
+        w = x.w
+        say(f"enqueue {w.name} on its own stream")
+        with torch.cuda.stream(s):
+            q, k, v, do = (to_dev(x, n) for n in ("q", "k", "v", "do"))
+            out = torch.empty_like(q)
+            lse = torch.empty((w.B, w.H, w.S), dtype=torch.float32, device="cuda")
+            delta = torch.empty_like(lse)
+            dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+            xfa.xfa_fwd(q, k, v, out, lse, w.sm_scale, w.causal)
+            xfa.xfa_bwd_preprocess(out, do, delta, w.sm_scale, w.causal)
+            xfa.xfa_bwd(q, k, v, do, lse, delta, dq, dk, dv, w.sm_scale, w.causal)
+        live.append(dict(out=out, lse=lse, delta=delta, dq=dq, dk=dk, dv=dv))
+    torch.cuda.synchronize()
+    for x, ts, ref in zip(xs, live, alone):
+        got = {n: host(t) for n, t in ts.items()}
+        for n in got:
+            np.testing.assert_array_equal(got[n], ref[n], err_msg=f"{x.w.name} {n}")
+        compare_head(x, got, x.w.BH - 1)
+
+
 def test_empty_and_error_paths():
     q = torch.zeros((1, 1, 0, 64), dtype=torch.bfloat16, device="cuda")
     out, lse = xfa.forward(q, q, q)
