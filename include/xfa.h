@@ -59,7 +59,7 @@ typedef enum {
 typedef enum {
   XFA_OK = 0,
   XFA_ERR_INVALID_ARGUMENT = 1, /* null or misaligned pointer, negative size, bad scale/causal/dtype */
-  XFA_ERR_UNSUPPORTED = 2,      /* hd not in {16,32,64,128}, S > 2^30, (S+256)*hd*4 >= 2^31, or too many workgroups */
+  XFA_ERR_UNSUPPORTED = 2,      /* hd not in {16,32,64,128}, S > 2^30, (S+256)*hd*4 >= 2^31, or B*H*ceil(S/128) >= 2^24 (workgroups of one dispatch) */
   XFA_ERR_HIP = 3               /* a kernel launch failed */
 } xfa_status_t;
 

@@ -119,6 +119,11 @@ def test_size_limits():
         assert _fwd(S=(1 << 22) - 200, hd=128, dtype=dtype) == UNSUP
         assert _fwd_drop(S=(1 << 22) - 200, hd=128, dtype=dtype) == UNSUP
         assert _bwd(S=(1 << 22) - 200, hd=128, dtype=dtype) == UNSUP
+        # one 1-D dispatch per kernel: B * H * ceil(S / 128) workgroups of 256
+        # work-items must stay below 2^24 (the work-item count is 32-bit)
+        for call in (_fwd, _pre, _bwd, _fwd_drop, _bwd_drop):
+            assert call(B=2, H=1 << 13, S=1 << 17, hd=16, dtype=dtype) == UNSUP
+            assert call(B=1, H=1 << 14, S=(1 << 17) - 127, hd=16, dtype=dtype) == UNSUP
 
 
 @pytest.mark.parametrize("call", [_fwd_drop, _bwd_drop])

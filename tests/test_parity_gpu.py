@@ -281,6 +281,39 @@ def test_concurrent_calls_on_two_streams():
         compare_head(x, got, x.w.BH - 1)
 
 
+def test_preprocess_beyond_one_grid_pass():
+    # D = rowsum(dO * O) over 33.6 M rows of bf16 hd 128: more rows than one
+    # capped grid of preprocess workgroups covers (2^20 workgroups of 32
+    # rows), so the rows past 2^25 come from a second pass of the grid.
+    # Inputs are drawn on the device; sampled rows, all rows of the second
+    # pass and the last rows are checked against float64 dot products.
+    B, H, S, hd = 8, 1025, 4096, 128
+    nrows = B * H * S
+    first_pass = (1 << 20) * 32
+    assert nrows > first_pass
+    say(f"preprocess over {nrows} rows (bf16, hd {hd})")
+    g = torch.Generator(device="cuda").manual_seed(91)
+    out = torch.randn((B, H, S, hd), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    do = torch.randn((B, H, S, hd), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    delta = torch.full((B, H, S), float("nan"), device="cuda")
+    xfa.xfa_bwd_preprocess(out, do, delta, 1.0 / math.sqrt(hd), True)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([rng.integers(0, first_pass, 4096),
+                                     np.arange(first_pass, nrows),
+                                     np.arange(nrows - 64, nrows)]))
+    idx = torch.from_numpy(rows).cuda()
+    o = out.view(nrows, hd)[idx].float().cpu().numpy().astype(np.float64)
+    d = do.view(nrows, hd)[idx].float().cpu().numpy().astype(np.float64)
+    got = delta.view(nrows)[idx].cpu().numpy().astype(np.float64)
+    ref = (o * d).sum(axis=1)
+    err = np.abs(got - ref) / (1e-6 + np.abs(o * d).sum(axis=1))
+    say(f"{len(rows)} rows checked, worst relative error {err.max():.3g}")
+    assert np.all(np.isfinite(got)) and err.max() <= 3e-5
+    del out, do, delta
+    torch.cuda.empty_cache()
+
+
 def test_empty_and_error_paths():
     q = torch.zeros((1, 1, 0, 64), dtype=torch.bfloat16, device="cuda")
     out, lse = xfa.forward(q, q, q)

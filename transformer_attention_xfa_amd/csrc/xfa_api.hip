@@ -24,8 +24,7 @@ xfa_status_t check_common(int64_t B, int64_t H, int64_t S, int64_t hd, float sca
   if (!(isfinite(scale) && scale > 0.f)) return XFA_ERR_INVALID_ARGUMENT;
   if (causal != 0 && causal != 1) return XFA_ERR_INVALID_ARGUMENT;
   if (hd != 16 && hd != 32 && hd != 64 && hd != 128) return XFA_ERR_UNSUPPORTED;
-  // the kernels index positions with int and launch one workgroup per
-  // (head, 32..128-row tile) on a 1-D grid
+  // the kernels index positions with int
   if (S > (int64_t(1) << 30)) return XFA_ERR_UNSUPPORTED;
   // one head of one fp32 tensor, plus the blocks the kernels stage past its
   // end (fewer than 256 rows), must stay below 2^31 bytes: the staging
@@ -33,7 +32,10 @@ xfa_status_t check_common(int64_t B, int64_t H, int64_t S, int64_t hd, float sca
   if ((S + 256) * hd * 4 > int64_t(INT32_MAX)) return XFA_ERR_UNSUPPORTED;
   if (B > 0 && H > INT64_MAX / B) return XFA_ERR_UNSUPPORTED;
   const int64_t BH = B * H;
-  if (BH > 0 && (S + 31) / 32 > int64_t(INT32_MAX) / BH) return XFA_ERR_UNSUPPORTED;
+  // each kernel of the three entry points but the preprocess launches one
+  // 256-thread workgroup per (head, 128-row tile) on a 1-D grid, and a
+  // dispatch counts its work-items in 32 bits
+  if (BH > 0 && (S + 127) / 128 > ((int64_t(1) << 24) - 1) / BH) return XFA_ERR_UNSUPPORTED;
   sh->BH = BH;
   sh->S = S;
   sh->hd = hd;

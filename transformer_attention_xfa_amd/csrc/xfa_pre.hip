@@ -14,6 +14,10 @@ namespace xfa {
 constexpr int kPreThreads = 256;
 constexpr int kPreUnroll = 2;
 
+// At most this many workgroups per launch (the dispatch counts work-items in
+// 32 bits); a larger problem loops over its rows in strides of the grid.
+constexpr int64_t kPreMaxGroups = int64_t(1) << 20;
+
 template <typename T, int HD>
 __global__ __launch_bounds__(kPreThreads) void bwd_pre_kernel(
     const T* __restrict__ O, const T* __restrict__ dO, float* __restrict__ Dl, int64_t nrows) {
@@ -22,29 +26,31 @@ __global__ __launch_bounds__(kPreThreads) void bwd_pre_kernel(
   constexpr int RPI = kPreThreads / LPR;           // rows per workgroup per unroll step
   const int tid = threadIdx.x;
   const int sub = tid % LPR;
-  const int64_t row0 = (int64_t)blockIdx.x * RPI * kPreUnroll + tid / LPR;
-
-  typename Vec16<T>::type a[kPreUnroll], b[kPreUnroll];
+  const int64_t stride = (int64_t)gridDim.x * RPI * kPreUnroll;
+  // the lanes of a row share row0, so they take every branch together
+  for (int64_t row0 = (int64_t)blockIdx.x * RPI * kPreUnroll + tid / LPR; row0 < nrows; row0 += stride) {
+    typename Vec16<T>::type a[kPreUnroll], b[kPreUnroll];
 #pragma unroll
-  for (int u = 0; u < kPreUnroll; ++u) {
-    const int64_t r = row0 + (int64_t)u * RPI;
-    if (r < nrows) {
-      a[u] = ld16(O + r * HD + sub * VE);
-      b[u] = ld16(dO + r * HD + sub * VE);
-    } else {
-      a[u] = typename Vec16<T>::type{};
-      b[u] = typename Vec16<T>::type{};
+    for (int u = 0; u < kPreUnroll; ++u) {
+      const int64_t r = row0 + (int64_t)u * RPI;
+      if (r < nrows) {
+        a[u] = ld16(O + r * HD + sub * VE);
+        b[u] = ld16(dO + r * HD + sub * VE);
+      } else {
+        a[u] = typename Vec16<T>::type{};
+        b[u] = typename Vec16<T>::type{};
+      }
     }
-  }
 #pragma unroll
-  for (int u = 0; u < kPreUnroll; ++u) {
-    float s = 0.f;
+    for (int u = 0; u < kPreUnroll; ++u) {
+      float s = 0.f;
 #pragma unroll
-    for (int e = 0; e < VE; ++e) s += (float)a[u][e] * (float)b[u][e];
+      for (int e = 0; e < VE; ++e) s += (float)a[u][e] * (float)b[u][e];
 #pragma unroll
-    for (int off = LPR / 2; off > 0; off >>= 1) s += __shfl_xor(s, off, LPR);
-    const int64_t r = row0 + (int64_t)u * RPI;
-    if (sub == 0 && r < nrows) Dl[r] = s;
+      for (int off = LPR / 2; off > 0; off >>= 1) s += __shfl_xor(s, off, LPR);
+      const int64_t r = row0 + (int64_t)u * RPI;
+      if (sub == 0 && r < nrows) Dl[r] = s;
+    }
   }
 }
 
@@ -53,7 +59,7 @@ static hipError_t launch_pre_t(const PreArgs& a) {
   constexpr int LPR = HD / Vec16<T>::N;
   constexpr int rows_per_wg = (kPreThreads / LPR) * kPreUnroll;
   const int64_t nrows = a.BH * a.S;
-  const int64_t nwg = (nrows + rows_per_wg - 1) / rows_per_wg;
+  const int64_t nwg = min((nrows + rows_per_wg - 1) / rows_per_wg, kPreMaxGroups);
   hipLaunchKernelGGL((bwd_pre_kernel<T, HD>), dim3((unsigned)nwg), dim3(kPreThreads), 0, a.stream,
                      (const T*)a.out, (const T*)a.dout, a.delta, nrows);
   return hipGetLastError();
