@@ -207,6 +207,33 @@ def test_edge_shapes(dtype, hd, causal):
             compare_head(x, g, bh)
 
 
+# A seeded sweep of shapes drawn at random (every dtype, head dim and mode,
+# lengths with ragged tails, odd head counts): a random head and the last one
+# of each against the oracle, the invariants over all heads.
+def _sweep_cases(n=24, seed=2024):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        dtype = ("f32", "bf16")[i % 2]
+        hd = (16, 32, 64, 128)[(i // 2) % 4]
+        causal = bool((i // 8) % 2 == 0)
+        B, H = int(rng.integers(1, 4)), int(rng.integers(1, 6))
+        S = int(rng.integers(2, 701))
+        cases.append((dtype, B, H, S, hd, causal, int(rng.integers(0, B * H))))
+    return cases
+
+
+@pytest.mark.parametrize("dtype,B,H,S,hd,causal,bh", _sweep_cases())
+def test_random_shape_sweep(dtype, B, H, S, hd, causal, bh):
+    w = workloads.Workload(f"sweep_{dtype}_b{B}h{H}_s{S}_hd{hd}_{'c' if causal else 'f'}", dtype, B, H, S, hd,
+                           seed=5000 + 7 * S + hd, causal=causal, do_std=1.0 if dtype == "f32" else 0.1)
+    x = workloads.make_inputs(w)
+    g = run_gpu(x)
+    for b in sorted({bh, w.BH - 1}):
+        compare_head(x, g, b)
+    check_invariants(x, g)
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_zero_query_is_uniform_attention(dtype):
     # Q = 0: out_i is the mean of V_0..V_i and L_i = ln(i+1)
