@@ -481,6 +481,11 @@ __device__ __forceinline__ void query_role(const BwdParams<T>& p, int bh, int qq
   // blocks [nm, nb) cross the diagonal of this workgroup's queries
   const int nm = p.causal ? q0 / NB : nb;
   const int nl = nb - 1;
+  // last key block any query of this wave sees: from iteration n_wave + 1
+  // on (blocks n and n+1 both past it) the wave only keeps the block ring
+  // going (its strips, the wait and the barrier, as many as the other waves)
+  // and leaves the other workgroup on its SIMD the cycles
+  const int n_wave = p.causal ? __builtin_amdgcn_readfirstlane(min(q0 + 32 * w + 31, S - 1) / NB) : nl;
 
   constexpr int NBUF = QB::NBUF;
   auto buf = [&](int n) { return QB(smem + (size_t)((unsigned)n % NBUF) * QB::BYTES); };
@@ -650,8 +655,15 @@ __device__ __forceinline__ void query_role(const BwdParams<T>& p, int bh, int qq
       __syncthreads();
     };
     Pipe::run(body, std::false_type{}, n, min(nm, nl), par);
-    Pipe::run(body, std::true_type{}, n, nl, par);
-    pipe.last(finish, nl >= nm, nl, par);
+    Pipe::run(body, std::true_type{}, n, min(nl, n_wave + 1), par);
+    for (; n < nl; ++n) {
+      const uint32_t fb = smem0 + (uint32_t)((unsigned)(n + NBUF - 1) % NBUF) * QB::BYTES;
+#pragma unroll
+      for (int t = 0; t < NPW; ++t) dma.issue_one(fb, (n + NBUF - 1) * NB, t);
+      wait_vm<(NBUF - 3) * NPW>();
+      __syncthreads();
+    }
+    if (nl <= n_wave) pipe.last(finish, nl >= nm, nl, par);
   } else {
     // fp32: one block per iteration, score and gradient contractions back
     // to back

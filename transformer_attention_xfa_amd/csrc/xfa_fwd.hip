@@ -84,6 +84,11 @@ __global__ __launch_bounds__(NW * 64, (sizeof(T) == 2 ? 2 : 1)) void fwd_kernel(
   const int nl = causal ? q_last / NB : (S + NB - 1) / NB - 1;
   const int nm = causal ? q0 / NB : (S % NB ? nl : nl + 1);
   const int key_lim = causal ? min(qi, S - 1) : S - 1;   // last key this lane's query sees
+  // last key block any query of this wave sees: from iteration n_wave + 1
+  // on (blocks n and n+1 both past it) the wave only keeps the block ring
+  // going (its strips, the wait and the barrier, as many as the other waves)
+  // and leaves the other workgroup on its SIMD the cycles
+  const int n_wave = causal ? __builtin_amdgcn_readfirstlane(min(q0 + 32 * w + 31, S - 1) / NB) : nl;
 
   // Q fragments: B operand of S^T = K . Q^T (column = query, natural d order)
   const rsrc_t rQ = make_rsrc(Q + hoff, head_bytes);
@@ -306,8 +311,15 @@ __global__ __launch_bounds__(NW * 64, (sizeof(T) == 2 ? 2 : 1)) void fwd_kernel(
       __syncthreads();
     };
     Pipe::run(body, std::false_type{}, n, min(nm, nl), par);
-    Pipe::run(body, std::true_type{}, n, nl, par);
-    pipe.last(finish, nl >= nm, nl, par);
+    Pipe::run(body, std::true_type{}, n, min(nl, n_wave + 1), par);
+    for (; n < nl; ++n) {
+      const uint32_t fb = smem0 + (uint32_t)((unsigned)(n + NBUF - 1) % NBUF) * FB::BYTES;
+#pragma unroll
+      for (int t = 0; t < NPW; ++t) dma.issue_one(fb, (n + NBUF - 1) * NB, t);
+      wait_vm<(NBUF - 3) * NPW>();
+      __syncthreads();
+    }
+    if (nl <= n_wave) pipe.last(finish, nl >= nm, nl, par);
   } else {
     // fp32: one block per iteration
 #pragma unroll
