@@ -130,7 +130,7 @@ __global__ __launch_bounds__(NW * 64, (sizeof(T) == 2 ? 2 : 1)) void fwd_kernel(
   };
   // mask (keys past the query or past the sequence end), block maximum and
   // the rescale of the running state when the reference moves
-  auto prepare = [&](auto masked, int n, f32x16& s) {
+  auto prepare = [&](auto masked, int n, f32x16& s) __attribute__((always_inline)) {
     if constexpr (decltype(masked)::value) {
       const int rel = key_lim - (n * NB + 4 * h);
 #pragma unroll
@@ -213,7 +213,7 @@ __global__ __launch_bounds__(NW * 64, (sizeof(T) == 2 ? 2 : 1)) void fwd_kernel(
   };
   // the whole of block n: weights, row sum and O^T += V^T . P^T (the fourth
   // argument, the pipeline's second tile, is unused here)
-  auto finish = [&](auto masked, int n, f32x16 s, const f32x16&) {
+  auto finish = [&](auto masked, int n, f32x16 s, const f32x16&) __attribute__((always_inline)) {
     FB b = buf(n);
     prepare(masked, n, s);
     const uint64_t bg = block_g(n);
