@@ -276,6 +276,26 @@ def test_nondefault_stream_and_repeatability():
         compare_head(x, g1, bh)
 
 
+# fp32 cases keep scale * sqrt(hd) below 1, the logit size of the default
+# scale, where the fp32 tolerances hold (the fp32 rounding of a score grows
+# with its size); each differs from 1/sqrt(hd) by a factor of 2.5 or more.
+@pytest.mark.parametrize("dtype,hd,causal,scale", [
+    ("f32", 64, True, 0.05), ("f32", 128, False, 0.03), ("f32", 32, True, 0.07),
+    ("bf16", 128, True, 0.03), ("bf16", 64, False, 0.3), ("bf16", 16, True, 1.0),
+    ("bf16", 128, True, 2.0),
+])
+def test_scale_other_than_default(dtype, hd, causal, scale):
+    # the softmax scale enters the exponent (scale * log2 e) and the dK and
+    # dQ stores; the other tests use 1/sqrt(hd)
+    w = workloads.Workload(f"scale{scale}_{dtype}_hd{hd}_{'c' if causal else 'f'}", dtype, 1, 3, 333, hd,
+                           seed=6000 + hd, causal=causal, scale=scale, do_std=1.0 if dtype == "f32" else 0.1)
+    x = workloads.make_inputs(w)
+    g = run_gpu(x)
+    for bh in range(w.BH):
+        compare_head(x, g, bh)
+    check_invariants(x, g)
+
+
 def test_concurrent_calls_on_two_streams():
     # The entry points keep no state between calls: two problems enqueued on
     # two streams at once, nothing ordering one against the other, give each
