@@ -361,6 +361,31 @@ def test_preprocess_beyond_one_grid_pass():
     torch.cuda.empty_cache()
 
 
+def test_binding_rejects_mismatched_tensors():
+    # the binding checks layout, shape and dtype itself, before any launch
+    q = torch.zeros((1, 2, 64, 64), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty_like(q)
+    lse = torch.empty((1, 2, 64), dtype=torch.float32, device="cuda")
+    bad = [
+        (q.transpose(2, 3), q, q, out, lse, "contiguous"),                      # non-contiguous q
+        (q, torch.zeros((1, 2, 32, 64), dtype=q.dtype, device="cuda"), q, out, lse, "shape"),  # k of another length
+        (q, q, q.float(), out, lse, "dtype"),                                   # v in another dtype
+        (q, q, q, out[:, :1], lse, "shape"),                                    # out of another shape
+        (q, q, q, out, lse.to(torch.bfloat16), "dtype"),                        # L not float32
+        (q, q, q, out, lse.cpu(), "GPU"),                                       # L on the host
+    ]
+    for a, b, c, o, l, what in bad:
+        with pytest.raises(ValueError, match=what):
+            xfa.xfa_fwd(a, b, c, o, l)
+    delta = torch.empty_like(lse)
+    dq = torch.empty_like(q)
+    with pytest.raises(ValueError, match="shape"):
+        xfa.xfa_bwd(q, q, q, q, lse, delta, torch.empty((1, 2, 8, 64), dtype=q.dtype, device="cuda"), dq, dq)
+    with pytest.raises(ValueError, match="contiguous"):
+        xfa.xfa_bwd_preprocess(out, q.transpose(2, 3), delta)
+    torch.cuda.synchronize()
+
+
 def test_empty_and_error_paths():
     q = torch.zeros((1, 1, 0, 64), dtype=torch.bfloat16, device="cuda")
     out, lse = xfa.forward(q, q, q)
