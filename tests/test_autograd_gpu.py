@@ -166,3 +166,24 @@ def test_double_backward_is_refused():
     g, = torch.autograd.grad(out.sum(), q, create_graph=True)
     with pytest.raises(RuntimeError):
         g.sum().backward()
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_views_of_a_packed_projection(dtype):
+    # q, k, v as strided views of one [B, S, 3, H, hd] projection (the usual
+    # head split): the op takes them as they are, and the gradient reaching
+    # the packed tensor equals that of the same op on contiguous copies
+    B, S, H, hd = 2, 200, 3, 64
+    g = torch.Generator(device="cuda").manual_seed(17)
+    qkv = torch.randn((B, S, 3, H, hd), generator=g, device="cuda").to(dtype).requires_grad_(True)
+    do = torch.randn((B, H, S, hd), generator=g, device="cuda").to(dtype)
+    q, k, v = (qkv[:, :, i].permute(0, 2, 1, 3) for i in range(3))
+    assert not q.is_contiguous()
+    out = xfa.flash_attention(q, k, v)
+    (gp,) = torch.autograd.grad(out, (qkv,), grad_outputs=do)
+    ref = qkv.detach().clone().requires_grad_(True)
+    qc, kc, vc = (ref[:, :, i].permute(0, 2, 1, 3).contiguous() for i in range(3))
+    out_c = xfa.flash_attention(qc, kc, vc)
+    (gr,) = torch.autograd.grad(out_c, (ref,), grad_outputs=do)
+    assert torch.equal(out, out_c)
+    assert torch.equal(gp, gr)
